@@ -1,0 +1,292 @@
+"""Pins of the oracle's quantize step against what the pages and mathematics fix.
+
+Every expected value here comes from somewhere other than the oracle: the
+table printed on the "Bit Layout" page, the E2M1 value formula of the same
+page, PyTorch's independent float8_e4m3fn codec, exact rational arithmetic
+(``fractions.Fraction``) or a hand derivation stored in ``tests/golden``.
+"""
+import json
+import math
+import os
+import struct
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import mx_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def f32_from_bits(b: int) -> float:
+    return struct.unpack("<f", struct.pack("<I", b))[0]
+
+
+def bits_of(v: float) -> int:
+    return struct.unpack("<I", struct.pack("<f", v))[0]
+
+
+def one_block(head, elem_pad=32):
+    x = np.zeros((1, elem_pad), dtype=np.float32)
+    x[0, :len(head)] = np.array(head, dtype=np.float32)
+    return x
+
+
+def unpacked(codes, elem):
+    return O.unpack_nibbles(codes) if elem == O.E2M1 else codes
+
+
+# ---------------------------------------------------------------- grids
+def test_e2m1_table_matches_printed_table():
+    rows = [l for l in open(os.path.join(GOLDEN, "e2m1_table.txt")) if not l.startswith("#")]
+    printed = np.array([float(r) for r in rows if r.strip()])
+    assert np.array_equal(O.e2m1_magnitudes(), printed)
+
+
+def test_e2m1_table_matches_bit_formula():
+    # "Bit Layout", "The E2M1 element": bias 1; normal (E>0) is 2^(E-1)(1+M/2),
+    # subnormal (E=0) is M/2.
+    for c in range(8):
+        e, m = c >> 1, c & 1
+        v = 2.0 ** (e - 1) * (1 + m / 2) if e else m / 2
+        assert O.e2m1_magnitudes()[c] == v
+
+
+def test_e4m3_grid_matches_torch_float8_decoder():
+    dec = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    grid = O.e4m3_magnitudes()
+    assert grid.shape == (127,)
+    assert np.array_equal(grid, dec[:127])
+    assert math.isnan(dec[127])
+    assert np.all(np.diff(grid) > 0)
+    assert grid[-1] == 448.0 and grid[1] == 2.0 ** -9
+
+
+# ------------------------------------------------------ worked examples
+def _golden_cases():
+    with open(os.path.join(GOLDEN, "worked_examples.json")) as f:
+        d = json.load(f)
+    return {k: v for k, v in d.items() if k.endswith("_block")}
+
+
+@pytest.mark.parametrize("name", sorted(_golden_cases()))
+def test_worked_examples(name):
+    case = _golden_cases()[name]
+    elem = O.E2M1 if case["elem"] == "E2M1" else O.E4M3
+    if "x_head_bits" in case:
+        head = [f32_from_bits(int(b, 16)) for b in case["x_head_bits"]]
+    else:
+        head = case["x_head"]
+    x = one_block(head, case["pad_zeros_to"])
+    codes, scales = O.quantize(x, elem)
+    assert int(scales[0, 0]) == case["scale_byte"]
+    u = unpacked(codes, elem)[0]
+    n = len(case["codes_head"])
+    assert u[:n].tolist() == case["codes_head"]
+    assert not u[n:].any()
+    if "packed_head" in case:
+        assert codes[0, :len(case["packed_head"])].tolist() == case["packed_head"]
+    if "decoded_head" in case:
+        y = O.dequantize(codes, scales, elem, 32)[0]
+        exp = np.array(case["decoded_head"], dtype=np.float32)
+        assert np.array_equal(y[:len(exp)].view(np.uint32), exp.view(np.uint32))
+
+
+# ------------------------------------------------------ exact exponent
+def _floor_log2_exact(v: float) -> int:
+    """floor(log2 v) of a positive float via exact rationals (independent of frexp)."""
+    q = Fraction(v)
+    n, d = q.numerator, q.denominator
+    k = n.bit_length() - d.bit_length()
+    # adjust so that 2^k <= q < 2^(k+1)
+    while Fraction(2) ** k > q:
+        k -= 1
+    while Fraction(2) ** (k + 1) <= q:
+        k += 1
+    return k
+
+
+@pytest.mark.parametrize("elem,emax", [(O.E2M1, 2), (O.E4M3, 8)])
+def test_scale_byte_exact_at_every_binade_edge(elem, emax):
+    amaxes = []
+    for k in range(-149, 128):
+        p = math.ldexp(1.0, k)
+        amaxes.append(p)
+        below = np.nextafter(np.float32(p), np.float32(0))
+        if below > 0:
+            amaxes.append(float(below))
+        above = np.nextafter(np.float32(p), np.float32(np.inf))
+        if np.isfinite(above):
+            amaxes.append(float(above))
+    amaxes.append(float(np.finfo(np.float32).max))
+    x = np.zeros((len(amaxes), 32), dtype=np.float32)
+    x[:, 0] = np.array(amaxes, dtype=np.float32)
+    _, scales = O.quantize(x, elem)
+    for i, a in enumerate(amaxes):
+        e = max(-127, min(127, _floor_log2_exact(float(np.float32(a))) - emax))
+        assert int(scales[i, 0]) == e + 127, (a, int(scales[i, 0]), e + 127)
+
+
+# ------------------------------------------------------ rounding
+def _nearest_exact(y: Fraction, grid) -> int:
+    best, bi = None, None
+    for j, g in enumerate(grid):
+        d = abs(y - Fraction(g))
+        if best is None or d < best:        # strict: ties keep the smaller index
+            best, bi = d, j
+    return bi
+
+
+def _anchor(elem):
+    # An element that forces e = 0: floor(log2 7) = 2 = emax(E2M1),
+    # floor(log2 511) = 8 = emax(E4M3).
+    return 7.0 if elem == O.E2M1 else 511.0
+
+
+@pytest.mark.parametrize("elem", [O.E2M1, O.E4M3])
+def test_rounding_brute_force_near_every_midpoint(elem):
+    grid = O.e2m1_magnitudes() if elem == O.E2M1 else O.e4m3_magnitudes()
+    vals = []
+    for j in range(len(grid) - 1):
+        mid = np.float32((grid[j] + grid[j + 1]) / 2)
+        vals += [mid, np.nextafter(mid, np.float32(0)), np.nextafter(mid, np.float32(1e9))]
+        vals += [np.float32(grid[j])]
+    top = np.float32(grid[-1])
+    vals += [top, np.nextafter(top, np.float32(1e9)), np.float32(_anchor(elem) * 0.999)]
+    rng = np.random.default_rng(7)
+    vals += list(rng.uniform(0, float(top) * 1.1, 3000).astype(np.float32))
+    vals = np.array(vals, dtype=np.float32)
+    nb = -(-len(vals) // 31)
+    x = np.zeros((nb, 32), dtype=np.float32)
+    x[:, 0] = _anchor(elem)
+    flat = np.zeros(nb * 31, dtype=np.float32)
+    flat[:len(vals)] = vals
+    x[:, 1:] = flat.reshape(nb, 31)
+    codes, scales = O.quantize(x, elem)
+    assert np.all(scales == 127)
+    u = unpacked(codes, elem)[:, 1:].reshape(-1)[:len(vals)]
+    for v, c in zip(vals, u):
+        assert int(c) == _nearest_exact(Fraction(float(v)), grid), (float(v), int(c))
+
+
+def test_e4m3_rounding_agrees_with_torch_rne_away_from_ties():
+    # Away from exact midpoints, round-to-nearest-even (PyTorch's cast) and
+    # round-to-nearest with ties down pick the same code.
+    grid = O.e4m3_magnitudes()
+    mids = set(((grid[:-1] + grid[1:]) / 2).tolist())
+    rng = np.random.default_rng(11)
+    v = np.concatenate([rng.uniform(-460, 460, 200_000), rng.standard_normal(100_000) * 0.05])
+    v = v.astype(np.float32)
+    v = v[np.abs(v) <= 448]
+    v = v[[abs(float(t)) not in mids for t in v]]
+    v = v[v != 0]
+    nb = len(v) // 31
+    v = v[:nb * 31]
+    x = np.zeros((nb, 32), dtype=np.float32)
+    x[:, 0] = 511.0
+    x[:, 1:] = v.reshape(nb, 31)
+    codes, _ = O.quantize(x, O.E4M3)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codes[:, 1:].reshape(-1), ref)
+
+
+def test_ties_go_to_smaller_index_e2m1():
+    x = one_block([7.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    codes, s = O.quantize(x, O.E2M1)
+    assert int(s[0, 0]) == 127
+    assert O.unpack_nibbles(codes)[0, 1:8].tolist() == [0, 1, 2, 3, 4, 5, 6]
+
+
+def test_saturation():
+    x = one_block([7.9, 6.5, 6.01])
+    codes, _ = O.quantize(x, O.E2M1)
+    assert O.unpack_nibbles(codes)[0, :3].tolist() == [7, 7, 7]
+    x = one_block([511.0, 470.0, 464.0001, 448.5])
+    codes, s = O.quantize(x, O.E4M3)
+    assert int(s[0, 0]) == 127 and codes[0, :4].tolist() == [0x7E] * 4
+
+
+def test_sign_rule_negative_zero_and_tiny_negatives():
+    x = one_block([4.0, -0.0, -1e-6, -0.2, -0.3])
+    codes, _ = O.quantize(x, O.E2M1)
+    assert O.unpack_nibbles(codes)[0, :5].tolist() == [6, 0, 8, 8, 9]
+    x = one_block([256.0, -0.0, -1e-9])
+    codes, _ = O.quantize(x, O.E4M3)
+    assert codes[0, :3].tolist() == [0x78, 0x00, 0x80]
+
+
+def test_nonfinite_blocks_reading():
+    # Reading: a block holding NaN or Inf gets scale 0xFF and zero codes
+    # (parity unpinned by the pages; E8M0's 0xFF is the only NaN encoding).
+    x = np.zeros((3, 64), dtype=np.float32)
+    x[0, 3] = np.nan
+    x[1, 40] = np.inf
+    x[2, 0] = -np.inf
+    x[:, 10] = 1.0
+    x[:, 50] = 1.0
+    for elem in (O.E2M1, O.E4M3):
+        codes, s = O.quantize(x, elem)
+        assert s.tolist() == [[255, 127 - (2 if elem == O.E2M1 else 8)],
+                              [127 - (2 if elem == O.E2M1 else 8), 255],
+                              [255, 127 - (2 if elem == O.E2M1 else 8)]]
+        u = unpacked(codes, elem)
+        assert not u[0, :32].any() and not u[1, 32:].any() and not u[2, :32].any()
+
+
+def test_shape_rule_rejects_ragged_blocks():
+    with pytest.raises(ValueError):
+        O.quantize(np.zeros((2, 48), np.float32), O.E2M1)
+
+
+def test_storage_matches_page_figures():
+    d = dict(l.split() for l in open(os.path.join(GOLDEN, "storage.txt")) if not l.startswith("#"))
+    r, c = 64, 1024
+    bits = (O.codes_bytes(r, c, O.E2M1) + O.num_scale_blocks(r, c)) * 8
+    blocks = O.num_scale_blocks(r, c)
+    assert bits / blocks == int(d["bits_per_block"])
+    assert bits / (r * c) == float(d["bits_per_element"])
+    assert round(16 / (bits / (r * c)), 2) == float(d["reduction_vs_bf16"])
+    x = np.random.default_rng(0).standard_normal((r, c)).astype(np.float32)
+    codes, scales = O.quantize(x, O.E2M1)
+    assert codes.nbytes + scales.nbytes == bits // 8
+
+
+def test_packing_element0_low_nibble():
+    codes = np.array([[0x1, 0x2, 0xF, 0x8]], dtype=np.uint8)
+    assert O.pack_nibbles(codes).tolist() == [[0x21, 0x8F]]
+    assert np.array_equal(O.unpack_nibbles(O.pack_nibbles(codes)), codes)
+
+
+@pytest.mark.parametrize("elem", [O.E2M1, O.E4M3])
+def test_requantize_is_idempotent(elem):
+    # The scale's exponent of a re-quantized block is unchanged: y_amax in
+    # [2^emax, 2^(emax+1)) rounds to a grid value in the same binade.
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal((64, 256)) * np.exp(rng.uniform(-20, 20, (64, 1)))).astype(np.float32)
+    c1, s1 = O.quantize(x, elem)
+    y = O.dequantize(c1, s1, elem, 256)
+    c2, s2 = O.quantize(y, elem)
+    assert np.array_equal(s1, s2)
+    u1, u2 = unpacked(c1, elem), unpacked(c2, elem)
+    neg0 = 0x8 if elem == O.E2M1 else 0x80
+    u1 = np.where(u1 == neg0, 0, u1)
+    assert np.array_equal(u1, u2)
+
+
+@pytest.mark.parametrize("elem", [O.E2M1, O.E4M3])
+def test_quantize_error_within_half_grid_step(elem):
+    # The round-trip error of every element is at most half of the local grid
+    # step times the block scale (or the saturation gap for the top binade).
+    grid = O.e2m1_magnitudes() if elem == O.E2M1 else O.e4m3_magnitudes()
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((32, 512)).astype(np.float32)
+    c, s = O.quantize(x, elem)
+    y = O.dequantize(c, s, elem, 512).astype(np.float64)
+    scale = np.repeat(np.ldexp(1.0, s.astype(np.int64) - 127), 32, axis=1)
+    t = np.abs(x.astype(np.float64)) / scale
+    j = np.clip(np.searchsorted(grid, t) , 1, len(grid) - 1)
+    step = grid[j] - grid[j - 1]
+    bound = np.where(t > grid[-1], t - grid[-1], step / 2) * scale
+    assert np.all(np.abs(y - x) <= bound + 0.0)
