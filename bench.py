@@ -1,0 +1,300 @@
+"""Benchmark of the MX hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one pass of the codec over the 8192x8192 MXFP4 weight workload
+(N(0, 0.02), 0.1% outliers x50): mx_quantize (f32 -> E2M1 codes + E8M0
+scales) followed by mx_dequantize (back to f32).  `value` is the algorithmic
+HBM traffic of the step (2 x 4.53125 B/element) divided by the step time, in
+GB/s.  Inputs are resident in HBM before the timed region; consecutive steps
+rotate over four copies of the workload (4 x 256 MiB of f32, larger than the
+256 MiB Infinity Cache) so that no step reads what the previous one left in
+the caches.
+
+The block-matmul workloads are timed in the same run and reported under
+"parts": the decode-shaped MXFP4 x MXFP4 16x4096x4096 product (HBM-bound),
+the MXFP8 8192^3 product and the prefill linear layer (2048x8192 activations
+quantized on the fly to E4M3, times MXFP4 weights 28672x8192), each with its
+roofline.  Kernel durations come from HIP events recorded on the stream the
+kernels run on.  The CPU oracle is timed on a bounded sample of the step's
+workload as `cpu_baseline`.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MX quantize/dequant GB/s (% HBM peak); block_matmul TFLOP/s (% MX MFMA peak)"
+HBM_PEAK_GBS = 8000.0
+PEAK_TFLOPS = {"fp4": 10100.0, "fp8": 5000.0}
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def codec_bytes(rows: int, cols: int, elem_bytes: float) -> int:
+    """Algorithmic HBM bytes of one quantize (or dequantize) of [rows, cols]:
+    4 B of f32 per element plus the codes and one scale byte per 32."""
+    n = rows * cols
+    return int(n * 4 + n * elem_bytes + n // 32)
+
+
+def matmul_bytes(M, N, K, a_bytes, b_bytes, accumulate=False) -> int:
+    return int(M * K * a_bytes + M * K // 32 + N * K * b_bytes + N * K // 32 +
+               M * N * 4 * (2 if accumulate else 1))
+
+
+def source_hash(*names: str) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "bit_gemm_mx_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, src: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(PROFILE_DIR, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    e = d.get(kernel)
+    if not e or e.get("source_sha256_16") != source_hash(src):
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+class EventTimer:
+    """Per-kernel durations from HIP events on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def run(self, name, fn):
+        s = self.torch.cuda.Event(enable_timing=True)
+        e = self.torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        self.pairs.setdefault(name, []).append((s, e))
+
+    def mean_ms(self, name):
+        v = [s.elapsed_time(e) for s, e in self.pairs[name]]
+        return float(np.mean(v)), float(np.min(v))
+
+
+def bench_codec(mx, W, torch, steps, warmup):
+    rows = cols = 8192
+    x_host = W.weight_codec_case(rows, cols, seed=1002)
+    copies = 4
+    xs = [torch.from_numpy(x_host).cuda() for _ in range(copies)]
+    qs = [mx.empty_mx(rows, cols, mx.MX_E2M1, xs[0].device) for _ in range(copies)]
+    ys = [torch.empty_like(xs[0]) for _ in range(copies)]
+    torch.cuda.synchronize()
+
+    def step(i, timer=None):
+        j = i % copies
+        if timer is None:
+            mx.quantize(xs[j], mx.MX_E2M1, out=qs[j])
+            mx.dequantize(qs[j], out=ys[j])
+        else:
+            timer.run("quantize", lambda: mx.quantize(xs[j], mx.MX_E2M1, out=qs[j]))
+            timer.run("dequantize", lambda: mx.dequantize(qs[j], out=ys[j]))
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # A second pass over the same steps with per-kernel events.
+    timer = EventTimer(torch)
+    for i in range(steps):
+        step(i, timer)
+    torch.cuda.synchronize()
+    per_op = codec_bytes(rows, cols, 0.5)
+    q_ms, q_min = timer.mean_ms("quantize")
+    d_ms, d_min = timer.mean_ms("dequantize")
+    kernels = {
+        "quantize_e2m1": dict(ms=q_ms, min_ms=q_min, bytes=per_op, src="quantize.hip",
+                              kernel="quantize_kernel<1>"),
+        "dequantize_e2m1": dict(ms=d_ms, min_ms=d_min, bytes=per_op, src="dequantize.hip",
+                                kernel="dequantize_kernel<1>"),
+    }
+    del xs, qs, ys
+    torch.cuda.empty_cache()
+    return wall, 2 * per_op, kernels
+
+
+def progress(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def roofline_hbm(name, k):
+    gbs = k["bytes"] / (k["ms"] * 1e-3) / 1e9
+    return {"bound": "hbm", "kernel": name, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(name, k["src"]),
+            "algorithmic_bytes": k["bytes"], "avg_ms": round(k["ms"], 5)}
+
+
+def bench_matmuls(mx, W, torch, reps):
+    out = {}
+
+    def timed(name, fn, n):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        t = EventTimer(torch)
+        for _ in range(n):
+            t.run(name, fn)
+        torch.cuda.synchronize()
+        return t.mean_ms(name)
+
+    # decode-shaped MXFP4 x MXFP4
+    a, bt = W.decode_matmul_case()
+    at = mx.quantize(torch.from_numpy(a).cuda(), mx.MX_E2M1)
+    btt = mx.quantize(torch.from_numpy(bt).cuda(), mx.MX_E2M1)
+    c = torch.empty((16, 4096), dtype=torch.float32, device="cuda")
+    ms, mn = timed("decode", lambda: mx.block_matmul(at, btt, out=c), max(reps, 20))
+    flops = 2 * 16 * 4096 * 4096
+    byts = matmul_bytes(16, 4096, 4096, 0.5, 0.5)
+    gbs = byts / (ms * 1e-3) / 1e9
+    out["decode_mxfp4_16x4096x4096"] = {
+        "ms": round(ms, 5), "min_ms": round(mn, 5), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "algorithmic_bytes": byts}}
+    del at, btt, c
+
+    progress(f"decode-shaped matmul done: {ms:.4f} ms")
+    # MXFP8 x MXFP8 8192^3
+    a, bt = W.square_fp8_case()
+    at = mx.quantize(torch.from_numpy(a).cuda(), mx.MX_E4M3)
+    btt = mx.quantize(torch.from_numpy(bt).cuda(), mx.MX_E4M3)
+    del a, bt
+    c = torch.empty((8192, 8192), dtype=torch.float32, device="cuda")
+    ms, mn = timed("fp8", lambda: mx.block_matmul(at, btt, out=c), reps)
+    flops = 2 * 8192 ** 3
+    tf = flops / (ms * 1e-3) / 1e12
+    out["mxfp8_8192x8192x8192"] = {
+        "ms": round(ms, 4), "min_ms": round(mn, 4), "tflops": round(tf, 1),
+        "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_TFLOPS["fp8"],
+                     "unit": "TFLOP/s", "frac": round(tf / PEAK_TFLOPS["fp8"], 4)}}
+    del at, btt, c
+    torch.cuda.empty_cache()
+
+    progress(f"MXFP8 8192^3 matmul done: {ms:.3f} ms")
+    # prefill linear: quantize activations to E4M3, then E4M3 x E2M1
+    a, bt = W.prefill_linear_case()
+    ad = torch.from_numpy(a).cuda()
+    btt = mx.quantize(torch.from_numpy(bt).cuda(), mx.MX_E2M1)
+    del bt
+    aq = mx.empty_mx(2048, 8192, mx.MX_E4M3, ad.device)
+    c = torch.empty((2048, 28672), dtype=torch.float32, device="cuda")
+
+    def prefill():
+        mx.quantize(ad, mx.MX_E4M3, out=aq)
+        mx.block_matmul(aq, btt, out=c)
+
+    ms, mn = timed("prefill", prefill, reps)
+    qms, _ = timed("prefill_q", lambda: mx.quantize(ad, mx.MX_E4M3, out=aq), reps)
+    mms, _ = timed("prefill_mm", lambda: mx.block_matmul(aq, btt, out=c), reps)
+    progress(f"prefill linear done: {ms:.3f} ms")
+    flops = 2 * 2048 * 28672 * 8192
+    tf = flops / (ms * 1e-3) / 1e12
+    tfm = flops / (mms * 1e-3) / 1e12
+    out["prefill_e4m3xe2m1_2048x28672x8192"] = {
+        "ms": round(ms, 4), "min_ms": round(mn, 4), "tflops": round(tf, 1),
+        "quantize_ms": round(qms, 4), "matmul_ms": round(mms, 4),
+        "roofline": {"bound": "mfma", "kernel": "block_matmul", "achieved": round(tfm, 1),
+                     "peak": PEAK_TFLOPS["fp8"], "unit": "TFLOP/s",
+                     "frac": round(tfm / PEAK_TFLOPS["fp8"], 4)}}
+    del ad, btt, aq, c
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(W, rows=2048, cols=8192):
+    """The oracle, as it stands, on the first `rows` rows of the step's workload."""
+    from oracle import mx_oracle as O
+    x = W.weight_codec_case(8192, cols, seed=1002)[:rows].copy()
+    t0 = time.perf_counter()
+    c, s = O.quantize(x, O.E2M1)
+    O.dequantize(c, s, O.E2M1, cols)
+    dt = time.perf_counter() - t0
+    gbs = 2 * codec_bytes(rows, cols, 0.5) / dt / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"quantize + dequantize of rows 0..{rows - 1} of the 8192x8192 workload "
+                      f"({rows * cols} elements), single-threaded NumPy, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-matmul", action="store_true", help="time the codec step only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the MX hot path has no "
+              "multi-GPU mode in this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bit_gemm_mx_amd as mx
+    from bit_gemm_mx_amd import workloads as W
+
+    if not os.path.exists(mx.binding.LIB_PATH):
+        from bit_gemm_mx_amd.build import build
+        build()
+    mx.lib()
+    if not torch.cuda.is_available():
+        raise RuntimeError("no GPU visible: bench.py measures the HIP path only")
+    torch.cuda.set_device(0)
+
+    progress("codec step: quantize + dequantize of the 8192x8192 weight workload")
+    wall, step_bytes, kernels = bench_codec(mx, W, torch, args.steps, args.warmup)
+    progress(f"codec step done: {wall / args.steps * 1e3:.3f} ms/step")
+    ms_step = wall / args.steps * 1e3
+    value = step_bytes / (wall / args.steps) / 1e9
+    rooflines = {k: roofline_hbm(k, v) for k, v in kernels.items()}
+    dominant = max(kernels, key=lambda k: kernels[k]["ms"])
+    parts = {"codec_kernels": rooflines}
+    if not args.no_matmul:
+        parts.update(bench_matmuls(mx, W, torch, max(3, args.steps // 2)))
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "MXFP4 weight quantize + dequantize, fp32 8192x8192, "
+                               "N(0,0.02) with 0.1% outliers x50, blocks of 32 along the last axis",
+                   "rows": 8192, "cols": 8192, "elem": "E2M1", "block_size": 32, "seed": 1002,
+                   "step": "mx_quantize then mx_dequantize"},
+        "roofline": rooflines[dominant],
+        "parts": parts,
+    }
+    if not args.no_cpu:
+        progress("timing the CPU oracle on a sample")
+        line["cpu_baseline"] = cpu_baseline(W)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,190 @@
+"""ctypes binding of libmx (argument marshalling only).
+
+Every computation runs in the HIP kernels behind the C ABI declared in
+``include/libmx.h``; this module only checks tensor dtypes/devices/contiguity,
+allocates outputs with ``torch.empty`` on the tensors' device and passes raw
+pointers plus the current HIP stream.  There is no CPU path: if the shared
+library is missing or fails to load, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmx.so")
+
+MX_E2M1 = 1
+MX_E4M3 = 2
+BLOCK = 32
+ELEM_NAMES = {MX_E2M1: "E2M1", MX_E4M3: "E4M3"}
+
+_STATUS = {0: "MX_OK", 1: "MX_ERR_NULL", 2: "MX_ERR_SHAPE", 3: "MX_ERR_UNSUPPORTED",
+           4: "MX_ERR_ALIGN", 5: "MX_ERR_HIP"}
+
+_lib = None
+
+
+class LibMXError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmx.so (once) and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m bit_gemm_mx_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    p, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    L.mx_quantize.argtypes = [p, p, p, i64, i64, i32, i32, p]
+    L.mx_quantize.restype = i32
+    L.mx_dequantize.argtypes = [p, p, p, i64, i64, i32, i32, p]
+    L.mx_dequantize.restype = i32
+    L.mx_block_matmul.argtypes = [p, p, i32, p, p, i32, p, i64, i64, i64, i32, i32, p]
+    L.mx_block_matmul.restype = i32
+    L.mx_codes_bytes.argtypes = [i64, i64, i32]
+    L.mx_codes_bytes.restype = sz
+    L.mx_num_scale_blocks.argtypes = [i64, i64, i32]
+    L.mx_num_scale_blocks.restype = i64
+    L.mx_status_string.argtypes = [i32]
+    L.mx_status_string.restype = ctypes.c_char_p
+    L.mx_abi_version.argtypes = []
+    L.mx_abi_version.restype = i32
+    _lib = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise LibMXError(status, lib().mx_status_string(status).decode())
+
+
+# ----------------------------------------------------------------- raw ABI
+def mx_quantize(x_ptr, codes_ptr, scales_ptr, rows, cols, elem, block_size=BLOCK, stream=None):
+    _check(lib().mx_quantize(x_ptr, codes_ptr, scales_ptr, rows, cols, elem, block_size, stream))
+
+
+def mx_dequantize(codes_ptr, scales_ptr, y_ptr, rows, cols, elem, block_size=BLOCK, stream=None):
+    _check(lib().mx_dequantize(codes_ptr, scales_ptr, y_ptr, rows, cols, elem, block_size, stream))
+
+
+def mx_block_matmul(a_codes, a_scales, a_elem, b_codes, b_scales, b_elem, c, M, N, K,
+                    block_size=BLOCK, accumulate=0, stream=None):
+    _check(lib().mx_block_matmul(a_codes, a_scales, a_elem, b_codes, b_scales, b_elem, c,
+                                 M, N, K, block_size, accumulate, stream))
+
+
+def mx_codes_bytes(rows, cols, elem) -> int:
+    return int(lib().mx_codes_bytes(rows, cols, elem))
+
+
+def mx_num_scale_blocks(rows, cols, block_size=BLOCK) -> int:
+    return int(lib().mx_num_scale_blocks(rows, cols, block_size))
+
+
+def mx_abi_version() -> int:
+    return int(lib().mx_abi_version())
+
+
+def mx_status_string(status: int) -> str:
+    return lib().mx_status_string(status).decode()
+
+
+# ------------------------------------------------------------ torch layer
+def _stream_ptr(device):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _require(t, dtype, name):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on a GPU device, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+@dataclass
+class MXTensor:
+    """A block-scaled [rows, cols] tensor: element codes plus E8M0 scales.
+
+    codes: uint8 [rows, cols/2] (E2M1, element 2j in the low nibble of byte j)
+           or uint8 [rows, cols] (E4M3);  scales: uint8 [rows, cols/32].
+    """
+    codes: "object"
+    scales: "object"
+    rows: int
+    cols: int
+    elem: int
+
+    @property
+    def device(self):
+        return self.codes.device
+
+
+def empty_mx(rows: int, cols: int, elem: int, device) -> MXTensor:
+    import torch
+    nbytes = mx_codes_bytes(rows, cols, elem)
+    width = nbytes // rows if rows else 0
+    codes = torch.empty((rows, width), dtype=torch.uint8, device=device)
+    scales = torch.empty((rows, cols // BLOCK), dtype=torch.uint8, device=device)
+    return MXTensor(codes, scales, rows, cols, elem)
+
+
+def quantize(x, elem: int = MX_E2M1, out: MXTensor | None = None) -> MXTensor:
+    """float32 [rows, cols] GPU tensor -> MXTensor (mx_quantize)."""
+    import torch
+    _require(x, torch.float32, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [rows, cols]")
+    rows, cols = x.shape
+    if out is None:
+        out = empty_mx(rows, cols, elem, x.device)
+    _require(out.codes, torch.uint8, "codes")
+    _require(out.scales, torch.uint8, "scales")
+    mx_quantize(x.data_ptr(), out.codes.data_ptr(), out.scales.data_ptr(), rows, cols, elem,
+                BLOCK, _stream_ptr(x.device))
+    return out
+
+
+def dequantize(t: MXTensor, out=None):
+    """MXTensor -> float32 [rows, cols] GPU tensor (mx_dequantize)."""
+    import torch
+    _require(t.codes, torch.uint8, "codes")
+    _require(t.scales, torch.uint8, "scales")
+    if out is None:
+        out = torch.empty((t.rows, t.cols), dtype=torch.float32, device=t.codes.device)
+    _require(out, torch.float32, "out")
+    mx_dequantize(t.codes.data_ptr(), t.scales.data_ptr(), out.data_ptr(), t.rows, t.cols,
+                  t.elem, BLOCK, _stream_ptr(out.device))
+    return out
+
+
+def block_matmul(a: MXTensor, bt: MXTensor, out=None, accumulate: bool = False):
+    """C = [C +] A . B with A [M, K] and B given as B^T [N, K] (mx_block_matmul)."""
+    import torch
+    if a.cols != bt.cols:
+        raise ValueError(f"K mismatch: A has {a.cols}, B^T has {bt.cols}")
+    M, N, K = a.rows, bt.rows, a.cols
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs an existing out tensor")
+        out = torch.empty((M, N), dtype=torch.float32, device=a.codes.device)
+    _require(out, torch.float32, "out")
+    for t, n in ((a.codes, "a.codes"), (a.scales, "a.scales"), (bt.codes, "bt.codes"),
+                 (bt.scales, "bt.scales")):
+        _require(t, torch.uint8, n)
+    mx_block_matmul(a.codes.data_ptr(), a.scales.data_ptr(), a.elem, bt.codes.data_ptr(),
+                    bt.scales.data_ptr(), bt.elem, out.data_ptr(), M, N, K, BLOCK,
+                    1 if accumulate else 0, _stream_ptr(out.device))
+    return out

@@ -1,0 +1,121 @@
+// MX dequantize: E2M1 / E4M3 codes + E8M0 scales -> float32.
+//
+// Semantics follow the "Bit Layout" page (mxfp4community.com), sections
+// "The E8M0 shared scale" (value 2^(byte-127), byte 0xFF poisons the block to
+// NaN) and "Reference encode and decode" (sign x table[magnitude] x scale,
+// exact).  E4M3 codes 0x7F / 0xFF are f8E4M3FN NaN.
+//
+// Decoding without tables: placing the element's exponent and mantissa bits
+// at the top of a float32 mantissa field and multiplying by a power of two
+// reproduces the element value exactly (E2M1: magnitude bits << 22, times
+// 2^126; E4M3: magnitude bits << 20, times 2^120), subnormal element codes
+// included, because f32 arithmetic keeps denormals (IEEE mode, no flushing).
+// The second multiply by the block scale is exact as well.
+//
+// Work mapping mirrors the quantize kernel: 8 lanes per block, each lane
+// writes one 16-byte float4, so a wave's store instruction writes 1 KiB of
+// contiguous memory; kUnroll independent blocks per lane and iteration.
+#include "mx_internal.h"
+
+namespace mx {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+constexpr int kBlocksPerWaveIter = 8 * kUnroll;
+constexpr uint32_t kNaN = 0x7FC00000u;
+
+__device__ __forceinline__ float scale_value(uint32_t byte) {
+  // 2^(byte-127); byte 0 is the float32 subnormal 2^-127.
+  return __uint_as_float(byte ? (byte << 23) : 0x00400000u);
+}
+
+// Nibble n (sign in bit 3) of an E2M1 code -> float bits, scaled.
+__device__ __forceinline__ uint32_t decode_e2m1(uint32_t n, float scale) {
+  const float mag = __uint_as_float((n & 7u) << 22) * 0x1p126f;
+  return __float_as_uint(mag * scale) | ((n & 8u) << 28);
+}
+
+// Byte c of an E4M3 code -> float bits, scaled (NaN codes handled by caller).
+__device__ __forceinline__ uint32_t decode_e4m3(uint32_t c, float scale) {
+  const float mag = __uint_as_float((c & 0x7Fu) << 20) * 0x1p120f;
+  const uint32_t v = __float_as_uint(mag * scale) | ((c & 0x80u) << 24);
+  return (c & 0x7Fu) == 0x7Fu ? kNaN : v;
+}
+
+template <int ELEM>
+__global__ void __launch_bounds__(kThreads)
+dequantize_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                  float4* __restrict__ y, int64_t n_blocks) {
+  const int lane = threadIdx.x & 63;
+  const int sub = lane & 7;
+  const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
+  const int64_t n_waves = ((int64_t)gridDim.x * kThreads) >> 6;
+  const int64_t n_iter = (n_blocks + kBlocksPerWaveIter - 1) / kBlocksPerWaveIter;
+
+  for (int64_t it = wave; it < n_iter; it += n_waves) {
+    const int64_t blk0 = it * kBlocksPerWaveIter + (lane >> 3);
+    uint32_t w[kUnroll];
+    uint32_t sb[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t blk = blk0 + 8 * u;
+      if (blk < n_blocks) {
+        if (ELEM == kE2M1)
+          w[u] = reinterpret_cast<const uint16_t*>(codes)[blk * 8 + sub];
+        else
+          w[u] = reinterpret_cast<const uint32_t*>(codes)[blk * 8 + sub];
+        sb[u] = scales[blk];
+      } else {
+        w[u] = 0;
+        sb[u] = 127;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t blk = blk0 + 8 * u;
+      const float s = scale_value(sb[u]);
+      uint32_t o0, o1, o2, o3;
+      if (ELEM == kE2M1) {
+        o0 = decode_e2m1(w[u], s);
+        o1 = decode_e2m1(w[u] >> 4, s);
+        o2 = decode_e2m1(w[u] >> 8, s);
+        o3 = decode_e2m1(w[u] >> 12, s);
+      } else {
+        o0 = decode_e4m3(w[u] & 0xFFu, s);
+        o1 = decode_e4m3((w[u] >> 8) & 0xFFu, s);
+        o2 = decode_e4m3((w[u] >> 16) & 0xFFu, s);
+        o3 = decode_e4m3(w[u] >> 24, s);
+      }
+      if (sb[u] == 0xFFu) o0 = o1 = o2 = o3 = kNaN;
+      if (blk < n_blocks)
+        y[blk * 8 + sub] = make_float4(__uint_as_float(o0), __uint_as_float(o1),
+                                       __uint_as_float(o2), __uint_as_float(o3));
+    }
+  }
+}
+
+int grid_for(int64_t n_blocks) {
+  const int64_t iters = (n_blocks + kBlocksPerWaveIter - 1) / kBlocksPerWaveIter;
+  int64_t wgs = (iters + kThreads / 64 - 1) / (kThreads / 64);
+  const int64_t cap = 256 * 16;
+  return (int)(wgs < cap ? wgs : cap);
+}
+
+}  // namespace
+
+hipError_t launch_dequantize(const void* codes, const uint8_t* scales, float* y,
+                             int64_t n_blocks, int elem, hipStream_t stream) {
+  const int grid = grid_for(n_blocks);
+  const uint8_t* c = static_cast<const uint8_t*>(codes);
+  float4* y4 = reinterpret_cast<float4*>(y);
+  if (elem == kE2M1)
+    hipLaunchKernelGGL(dequantize_kernel<kE2M1>, dim3(grid), dim3(kThreads), 0, stream, c,
+                       scales, y4, n_blocks);
+  else
+    hipLaunchKernelGGL(dequantize_kernel<kE4M3>, dim3(grid), dim3(kThreads), 0, stream, c,
+                       scales, y4, n_blocks);
+  return hipGetLastError();
+}
+
+}  // namespace mx

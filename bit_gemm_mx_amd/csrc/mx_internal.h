@@ -1,0 +1,26 @@
+// Internal declarations shared by the libmx host layer and its HIP kernels.
+// Not part of the public interface (that is include/libmx.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mx {
+
+// Element formats, numbered as in the public header.
+enum Elem : int { kE2M1 = 1, kE4M3 = 2 };
+
+// Streaming codec kernels (quantize.hip, dequantize.hip).  n_blocks is
+// rows*cols/32; buffers are dense and 16-byte aligned.
+hipError_t launch_quantize(const float* x, void* codes, uint8_t* scales, int64_t n_blocks,
+                           int elem, hipStream_t stream);
+hipError_t launch_dequantize(const void* codes, const uint8_t* scales, float* y,
+                             int64_t n_blocks, int elem, hipStream_t stream);
+
+// Block-scaled matmul (block_matmul.hip).  C[M,N] (+)= A[M,K] . (B^T[N,K])^T.
+hipError_t launch_block_matmul(const void* a_codes, const uint8_t* a_scales, int a_elem,
+                               const void* b_codes, const uint8_t* b_scales, int b_elem,
+                               float* c, int64_t M, int64_t N, int64_t K, int accumulate,
+                               hipStream_t stream);
+
+}  // namespace mx

@@ -1,0 +1,140 @@
+/*
+ * libmx -- OCP Microscaling (MX) quantize / dequantize / block matmul on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Formats (all from the "Bit Layout" page, mxfp4community.com, unless noted):
+ *   - E2M1 element: 1 sign, 2 exponent (bias 1), 1 mantissa bit; the eight
+ *     magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}; no Inf, no NaN
+ *     (section "The E2M1 element").
+ *   - E4M3 element: f8E4M3FN, 1 sign, 4 exponent (bias 7), 3 mantissa bits,
+ *     largest finite magnitude 448, codes 0x7F/0xFF are NaN ("A Dialect Is a
+ *     Set of Co-Designed Decisions", section "The type: !mx.tensor").
+ *   - E8M0 scale: one unsigned byte per block, value 2^(byte-127); byte 0xFF
+ *     is NaN and turns every element of its block into NaN
+ *     (section "The E8M0 shared scale").
+ *   - A block is 32 contiguous elements along the last (reduction) axis
+ *     (section "Block structure and packing"; dialect page, "The block axis").
+ *
+ * Memory layouts (all row-major, dense, no padding between rows):
+ *   - x, y:    float32 [rows, cols]
+ *   - codes:   E2M1 -> uint8 [rows, cols/2], element 2j in the low nibble and
+ *              element 2j+1 in the high nibble of byte j (section "Block
+ *              structure and packing");  E4M3 -> uint8 [rows, cols].
+ *   - scales:  uint8 [rows, cols/32]; scale [r, j] covers x[r, 32j .. 32j+31].
+ *   - block_matmul takes B transposed, B^T [N, K], so that B's blocks also
+ *     run along K, its reduction axis (dialect page, "The block axis": the
+ *     block axis must be the reduction axis).  A matrix quantized with
+ *     mx_quantize in the [N, K] orientation is a valid B operand.
+ *
+ * Ownership and asynchrony: every pointer is a device pointer owned by the
+ * caller (e.g. from hipMalloc or torch.empty on the GPU).  libmx never
+ * allocates, frees or retains a pointer beyond the call.  Work is enqueued on
+ * `stream` (NULL = the default stream) and runs asynchronously: synchronize the
+ * stream before reading results on the host.  Functions are thread-safe.
+ *
+ * Errors: arguments are validated before anything is enqueued; on any error
+ * nothing is launched and nothing is written.  Validation is structural only
+ * (null pointers, sizes, divisibility, element type, block size, alignment);
+ * data never causes an error: a 0xFF scale decodes to NaN and a block of x
+ * holding NaN or Inf quantizes to scale 0xFF with zero codes.  A failed
+ * kernel launch returns MX_ERR_HIP.  Inputs and outputs must not overlap.
+ */
+#ifndef LIBMX_H
+#define LIBMX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LIBMX_ABI_VERSION 1
+#define MX_BLOCK_SIZE 32
+
+/* Same object as HIP's hipStream_t (a pointer to the runtime's stream). */
+typedef struct ihipStream_t *mx_stream_t;
+
+typedef enum {
+  MX_E2M1 = 1, /* MXFP4 element, packed two per byte */
+  MX_E4M3 = 2  /* MXFP8 element (f8E4M3FN), one per byte */
+} mx_elem_t;
+
+typedef enum {
+  MX_OK = 0,
+  MX_ERR_NULL = 1,        /* a required pointer is NULL                         */
+  MX_ERR_SHAPE = 2,       /* a size < 1, or cols / K not a multiple of 32        */
+  MX_ERR_UNSUPPORTED = 3, /* element type not E2M1/E4M3, or block_size != 32     */
+  MX_ERR_ALIGN = 4,       /* x / y / codes / c pointer not 16-byte aligned       */
+  MX_ERR_HIP = 5          /* the HIP runtime reported an error at launch         */
+} mx_status_t;
+
+/*
+ * mx_quantize -- float32 [rows, cols] -> element codes + E8M0 scales.
+ * Follows "Bit Layout", section "Reference encode and decode"; the dialect
+ * page, section "The four ops" (quantize_block).  Per block of 32:
+ *   amax = max |x_i|;  amax == 0 -> codes 0, scale byte 127;
+ *   e = clip(floor(log2 amax) - emax, -127, 127), floor taken exactly
+ *   (emax = 2 for E2M1, 8 for E4M3);  scale byte = e + 127;
+ *   code_i = index of the grid magnitude nearest to |x_i| / 2^e (ties to the
+ *   smaller magnitude, values above the grid saturate to its top)
+ *   | sign, where the sign bit is set iff x_i < 0 (so -0.0 gives code 0).
+ *   A block holding NaN or Inf gets scale byte 0xFF and zero codes.
+ * x: device float32 [rows, cols], 16-byte aligned (read).
+ * codes: device, mx_codes_bytes(rows, cols, elem) bytes, 16-byte aligned (written).
+ * scales: device, mx_num_scale_blocks(rows, cols, 32) bytes (written).
+ * block_size must be 32.
+ */
+mx_status_t mx_quantize(const float *x, void *codes, uint8_t *scales, int64_t rows,
+                        int64_t cols, mx_elem_t elem, int32_t block_size,
+                        mx_stream_t stream);
+
+/*
+ * mx_dequantize -- element codes + E8M0 scales -> float32 [rows, cols].
+ * Follows "Bit Layout", sections "The E8M0 shared scale" and "Reference
+ * encode and decode"; the dialect page, section "The four ops"
+ * (dequantize_block).  y = (-1)^s * grid[magnitude] * 2^(byte-127), exact;
+ * byte 0xFF -> every element of the block is NaN (bits 0x7FC00000), as are
+ * E4M3 NaN codes.  Layouts as mx_quantize; y is 16-byte aligned (written).
+ */
+mx_status_t mx_dequantize(const void *codes, const uint8_t *scales, float *y, int64_t rows,
+                          int64_t cols, mx_elem_t elem, int32_t block_size,
+                          mx_stream_t stream);
+
+/*
+ * mx_block_matmul -- C = [accumulate ? C : 0] + A . B on block-scaled operands.
+ * Follows the dialect page, sections "The four ops" (block_matmul, C += A.B),
+ * "The block axis" (each block scale is constant along the 32-run of K it
+ * multiplies, so it factors out of that partial sum) and "The accumulator
+ * operand" (C is both input and output, updated in place).
+ *   A:   a_codes [M, K or K/2] + a_scales [M, K/32], element type a_elem.
+ *   B^T: b_codes [N, K or K/2] + b_scales [N, K/32], element type b_elem.
+ *   C:   device float32 [M, N], 16-byte aligned; read only if accumulate != 0.
+ *   C[m,n] = sum_j 2^(sa[m,j]+sb[n,j]-254) * sum_{k in block j} qa[m,k]*qb[n,k]
+ * with float32 accumulation; a NaN scale or E4M3 NaN code in row m of A or
+ * row n of B^T makes C[m,n] NaN.  Any (a_elem, b_elem) pair of E2M1/E4M3.
+ */
+mx_status_t mx_block_matmul(const void *a_codes, const uint8_t *a_scales, mx_elem_t a_elem,
+                            const void *b_codes, const uint8_t *b_scales, mx_elem_t b_elem,
+                            float *c, int64_t M, int64_t N, int64_t K, int32_t block_size,
+                            int32_t accumulate, mx_stream_t stream);
+
+/* Bytes of the codes of a [rows, cols] tensor: rows*cols/2 (E2M1) or
+ * rows*cols (E4M3); 0 for an invalid element type or negative size. */
+size_t mx_codes_bytes(int64_t rows, int64_t cols, mx_elem_t elem);
+
+/* Number of E8M0 scales (one per block along the last axis): rows*cols/block_size;
+ * dialect page, section "The type: !mx.tensor".  0 for invalid arguments. */
+int64_t mx_num_scale_blocks(int64_t rows, int64_t cols, int32_t block_size);
+
+/* Static, NUL-terminated description of a status code. */
+const char *mx_status_string(mx_status_t status);
+
+/* LIBMX_ABI_VERSION of the built library. */
+int32_t mx_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBMX_H */

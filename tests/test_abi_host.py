@@ -1,0 +1,105 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched).
+
+* the shared library loads and exports every function include/libmx.h declares;
+* the size helpers follow the storage arithmetic of the "Bit Layout" page;
+* every validation error is returned before anything is enqueued (the
+  pointers passed here are never dereferenced: each call fails validation).
+"""
+import os
+import re
+
+import pytest
+
+from bit_gemm_mx_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libmx.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB_PATH):
+        from bit_gemm_mx_amd.build import build
+        build()
+    return B.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mx_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted([
+        "mx_abi_version", "mx_block_matmul", "mx_codes_bytes", "mx_dequantize",
+        "mx_num_scale_blocks", "mx_quantize", "mx_status_string"])
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_abi_version(L):
+    assert B.mx_abi_version() == 1
+
+
+def test_size_helpers(L):
+    assert B.mx_codes_bytes(256, 1024, B.MX_E2M1) == 131072
+    assert B.mx_codes_bytes(256, 1024, B.MX_E4M3) == 262144
+    assert B.mx_codes_bytes(4, 32, 9) == 0
+    assert B.mx_num_scale_blocks(256, 1024) == 8192
+    assert B.mx_num_scale_blocks(8192, 8192) == 2097152
+    assert B.mx_num_scale_blocks(3, 33) == 0
+    # 136 bits per block of 32 E2M1 elements ("Bit Layout", storage figure)
+    bits = (B.mx_codes_bytes(1, 32, B.MX_E2M1) + B.mx_num_scale_blocks(1, 32)) * 8
+    assert bits == 136
+
+
+def test_status_strings(L):
+    for s in range(6):
+        assert isinstance(B.mx_status_string(s), str) and B.mx_status_string(s)
+    assert B.mx_status_string(0) == "ok"
+
+
+# Fake, never-dereferenced device addresses.
+X, C, S, Y = 0x10000, 0x20000, 0x30000, 0x40000
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, C, S, 4, 64, 1, 32), 1),           # null x
+    ((X, 0, S, 4, 64, 1, 32), 1),           # null codes
+    ((X, C, 0, 4, 64, 1, 32), 1),           # null scales
+    ((X, C, S, 4, 64, 3, 32), 3),           # bad element type
+    ((X, C, S, 4, 64, 1, 16), 3),           # block size other than 32
+    ((X, C, S, 0, 64, 1, 32), 2),           # no rows
+    ((X, C, S, 4, 0, 1, 32), 2),            # no cols
+    ((X, C, S, 4, 48, 1, 32), 2),           # cols not a multiple of 32
+    ((X, C, S, -1, 64, 2, 32), 2),          # negative rows
+    ((X + 4, C, S, 4, 64, 1, 32), 4),       # misaligned x
+    ((X, C + 8, S, 4, 64, 2, 32), 4),       # misaligned codes
+])
+def test_codec_validation(L, args, status):
+    assert L.mx_quantize(*args, None) == status
+    x, c, s, r, k, e, bs = args
+    assert L.mx_dequantize(c, s, x, r, k, e, bs, None) == status
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(a=0), 1), (dict(sa=0), 1), (dict(b=0), 1), (dict(sb=0), 1), (dict(c=0), 1),
+    (dict(ae=0), 3), (dict(be=7), 3), (dict(bs=64), 3),
+    (dict(M=0), 2), (dict(N=0), 2), (dict(K=0), 2), (dict(K=100), 2), (dict(M=-3), 2),
+    (dict(a=X + 1), 4), (dict(b=C + 2), 4), (dict(c=Y + 4), 4),
+])
+def test_matmul_validation(L, over, status):
+    a = dict(a=X, sa=S, ae=1, b=C, sb=S + 4096, be=2, c=Y, M=16, N=16, K=128, bs=32, acc=0)
+    a.update(over)
+    assert L.mx_block_matmul(a["a"], a["sa"], a["ae"], a["b"], a["sb"], a["be"], a["c"],
+                             a["M"], a["N"], a["K"], a["bs"], a["acc"], None) == status
+
+
+def test_python_layer_rejects_cpu_tensors(L):
+    import torch
+    with pytest.raises(ValueError):
+        B.quantize(torch.zeros(4, 64))
