@@ -229,18 +229,26 @@ def bench_matmuls(mx, W, torch, reps):
     return out
 
 
-def cpu_baseline(W, rows=2048, cols=8192):
-    """The oracle, as it stands, on the first `rows` rows of the step's workload."""
+def cpu_baseline(W, cols=8192, min_seconds=10.0):
+    """The oracle, as it stands, on the step's workload: whole 8192x8192
+    quantize + dequantize passes, repeated until at least `min_seconds` of CPU
+    time have elapsed (single-threaded NumPy)."""
     from oracle import mx_oracle as O
-    x = W.weight_codec_case(8192, cols, seed=1002)[:rows].copy()
+    x = W.weight_codec_case(8192, cols, seed=1002)
+    rows = x.shape[0]
     t0 = time.perf_counter()
-    c, s = O.quantize(x, O.E2M1)
-    O.dequantize(c, s, O.E2M1, cols)
-    dt = time.perf_counter() - t0
-    gbs = 2 * codec_bytes(rows, cols, 0.5) / dt / 1e9
+    passes = 0
+    while True:
+        c, s = O.quantize(x, O.E2M1)
+        O.dequantize(c, s, O.E2M1, cols)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    gbs = passes * 2 * codec_bytes(rows, cols, 0.5) / dt / 1e9
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"quantize + dequantize of rows 0..{rows - 1} of the 8192x8192 workload "
-                      f"({rows * cols} elements), single-threaded NumPy, {dt:.1f} s"}
+            "sample": f"{passes} quantize + dequantize pass(es) over the whole 8192x8192 "
+                      f"workload, single-threaded NumPy, {dt:.1f} s"}
 
 
 def main():

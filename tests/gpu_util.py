@@ -55,22 +55,22 @@ def assert_matmul_close(got: np.ndarray, want: np.ndarray, mag: np.ndarray, rel:
     return worst
 
 
-def mfma_group_bound(a_dq: np.ndarray, b_dq: np.ndarray, group: int = 8) -> np.ndarray:
-    """Extra error allowed by the scaled-MFMA arithmetic measured on gfx950:
-    each aligned group of `group` consecutive K products is summed in fixed
-    point aligned to the group's largest product, truncating bits below
+def mfma_group_bound(a_dq: np.ndarray, b_dq: np.ndarray, rows, cols, group: int = 8) -> np.ndarray:
+    """Extra error allowed by the scaled-MFMA arithmetic measured on gfx950,
+    at the output elements (rows[i], cols[i]).
+
+    Each aligned group of `group` consecutive K products is summed in fixed
+    point aligned to the group's largest product, dropping bits below
     2^(E-14) (E = floor(log2 max |p|) in the group); the groups are then added
-    in fp32.  Per group the truncation error is < group * 2^(E-14) <= 2^(E-10)
-    for group = 8.  Returns sum over groups of 2^(E_g - 10), [M, N]."""
-    M, K = a_dq.shape
-    N = b_dq.shape[0]
-    out = np.zeros((M, N))
-    a = np.nan_to_num(np.abs(a_dq))
-    b = np.nan_to_num(np.abs(b_dq))
-    for m0 in range(0, M, 8):
-        p = a[m0:m0 + 8, None, :] * b[None, :, :]
-        gmax = p.reshape(p.shape[0], N, K // group, group).max(axis=-1)
+    in fp32.  Per group the error is < group * 2^(E-14) <= 2^(E-10) for
+    group = 8.  Returns sum over groups of 2^(E_g - 10) per element."""
+    K = a_dq.shape[1]
+    out = np.zeros(len(rows))
+    for s0 in range(0, len(rows), 256):
+        r, c = rows[s0:s0 + 256], cols[s0:s0 + 256]
+        p = np.nan_to_num(np.abs(a_dq[r] * b_dq[c]))
+        gmax = p.reshape(len(r), K // group, group).max(axis=-1)
         with np.errstate(divide="ignore"):
             e = np.floor(np.log2(gmax))
-        out[m0:m0 + 8] = np.where(gmax > 0, np.exp2(e - 10), 0.0).sum(axis=-1)
+        out[s0:s0 + 256] = np.where(gmax > 0, np.exp2(e - 10), 0.0).sum(axis=-1)
     return out
