@@ -22,6 +22,8 @@
 //     32x32x64 -> C[8(j/4) + 4g + (j%4)][l % 32], j = 0..15.
 // B^T rows use the same layout as A rows (B column n = B^T row n).  A 0xFF
 // scale or an E4M3 NaN code makes the affected outputs NaN in hardware.
+#include <type_traits>
+
 #include "mx_internal.h"
 
 namespace mx {
@@ -111,37 +113,45 @@ block_matmul_simple(const uint8_t* __restrict__ a, const uint8_t* __restrict__ s
 
 // ---------------------------------------------------------------------------
 // Tiled kernel: 256x256 output tile per workgroup of 4 waves (2 x 2), each
-// wave 128x128 = 4 x 4 tiles of the 32x32x64 scaled MFMA.  K advances in
-// stages of 128 elements: codes are staged in LDS (double-buffered, the next
-// stage prefetched into registers while the current one feeds the MFMAs) and
-// the scale bytes go straight from global memory to registers.
+// wave 128x128 = 4 x 4 tiles of the 32x32x64 scaled MFMA.
+//
+// K runs in stages of 128 elements (two MFMA K steps).  Code tiles are staged
+// straight into LDS by buffer loads that write LDS, kStages buffers deep; an
+// FP8 row of a stage is one whole 128-byte cache line.  Scale bytes are staged
+// the same way, 16 per row (512 K elements, a "scale chunk" of 4 stages) in
+// one load per row, double-buffered by chunk parity.  Every global load of the
+// main loop thus writes LDS and is covered by the explicit waits before the
+// barriers; operand and scale registers only wait on LDS reads.
 // ---------------------------------------------------------------------------
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kTM = 256, kTN = 256, kTK = 128, kTThreads = 256;
+constexpr int kChunkStages = 4;                   // stages per scale chunk
+constexpr int kScaleRowBytes = 16;                // scale bytes per row per chunk
+constexpr int kScaleBytes = 2 * 256 * kScaleRowBytes;  // A and B rows of one chunk
 
 template <int ELEM>
 struct Stage {
   static constexpr int kRowBytes = ELEM == kE2M1 ? kTK / 2 : kTK;  // 64 or 128
   static constexpr int kChunks = kRowBytes / 16;                     // 16-B chunks per row
+  static constexpr int kRowsPerLine = 256 / kRowBytes;               // rows per 256-B line
   static constexpr int kBytes = 256 * kRowBytes;                     // one 256-row tile
-  static constexpr int kLoads = 256 * kChunks / kTThreads;           // chunks per thread
-  static constexpr int kRowStep = kTThreads / kChunks;               // rows between a thread's chunks
+  static constexpr int kInstr = kBytes / 1024 / 4;                   // 1-KiB loads per wave
 };
 
 // LDS byte offset of 16-byte chunk c of row r of a staged tile.  Rows are
-// packed into 128-byte lines (one FP8 row or two FP4 rows per line) and the
-// chunk index within the line is XOR-swizzled with the line index, so that
-// eight lanes touching the same logical chunk of eight consecutive rows (an
-// MFMA operand read) or eight consecutive chunks (a staging write) address
-// eight different 16-byte bank groups.
+// packed into 256-byte lines (the width the LDS serves per clock: 64 banks of
+// 4 bytes, 16 lanes of a 16-byte read) and the chunk index within the line is
+// XOR-swizzled with the line index, so that the 16 lanes reading the same
+// logical chunk of 16 consecutive rows (an MFMA operand read) address 16
+// different 16-byte bank groups.
 template <int ELEM>
 __device__ __forceinline__ int lds_off(int r, int c) {
-  if (ELEM == kE4M3) return r * 128 + ((c ^ (r & 7)) << 4);
-  const int line = r >> 1;
-  const int q = ((r & 1) << 2) | c;
-  return line * 128 + ((q ^ (line & 7)) << 4);
+  using S = Stage<ELEM>;
+  const int line = r / S::kRowsPerLine;
+  const int q = (r % S::kRowsPerLine) * S::kChunks + c;
+  return line * 256 + ((q ^ (line % S::kChunks)) << 4);
 }
 
 // Buffer resource over `bytes` bytes at `base` (raw buffer: offsets are byte
@@ -154,46 +164,43 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 constexpr uint32_t kOutOfRange = 0x80000000u;  // past every resource used here
 
 // Stage one 256-row tile of codes straight into LDS with buffer loads that
-// write LDS directly (each wave instruction fills 1 KiB: lane i writes bytes
-// [16i, 16i+16) of it).  LDS position (line L, chunk p) must hold logical
-// chunk p ^ (L & 7) of its row (the swizzle of lds_off), so each lane fetches
-// that chunk from global memory.  Within one instruction, lane i covers line
-// 8j' + i/8 (j' = the instruction's index in the tile), so its row offset
-// inside the instruction and its chunk do not depend on j'.
+// write LDS directly (each wave instruction fills 1 KiB = 4 lines: lane i
+// writes bytes [16i, 16i+16) of it).  LDS position (line L, chunk p) must hold
+// logical chunk q = p ^ (L % kChunks) of row L * kRowsPerLine + q / kChunks, so
+// each lane fetches that chunk from global memory.  Lane i covers line
+// 4j + i/16 of instruction j; L % kChunks depends on the lane and, for 8 chunks
+// per row, on the parity of j, so two lane offsets are kept.
 template <int ELEM>
 struct Stager {
-  static constexpr int kInstr = Stage<ELEM>::kBytes / 1024 / 4;    // per wave
-  static constexpr int kRowsPerInstr = ELEM == kE4M3 ? 8 : 16;
-  uint32_t lane_off;   // row-in-instruction * row_bytes + 16 * chunk
-  uint32_t chunk16;    // 16 * chunk: byte of the chunk within the stage's row slice
-  uint32_t instr_step; // bytes between consecutive instructions' first rows
+  using S = Stage<ELEM>;
+  uint32_t lane_off[2];  // row-in-instruction * row_bytes + 16 * chunk (even / odd j)
+  uint32_t chunk16[2];   // 16 * chunk
+  uint32_t instr_step;   // bytes between consecutive instructions' first rows
 
   __device__ __forceinline__ Stager(uint32_t row_bytes, int lane) {
-    const int p = lane & 7, l8 = lane >> 3;
-    const int q = p ^ l8;
-    int r, c;
-    if (ELEM == kE4M3) {
-      r = l8;
-      c = q;
-    } else {
-      r = 2 * l8 + (q >> 2);
-      c = q & 3;
+#pragma unroll
+    for (int odd = 0; odd < 2; ++odd) {
+      const int line = 4 * odd + (lane >> 4);  // line within an 8-line period
+      const int q = (lane & 15) ^ (line % S::kChunks);
+      const int r = (lane >> 4) * S::kRowsPerLine + q / S::kChunks;
+      const int c = q % S::kChunks;
+      chunk16[odd] = 16u * c;
+      lane_off[odd] = (uint32_t)r * row_bytes + 16u * c;
     }
-    chunk16 = 16u * c;
-    lane_off = (uint32_t)r * row_bytes + chunk16;
-    instr_step = kRowsPerInstr * row_bytes;
+    instr_step = 4 * S::kRowsPerLine * row_bytes;
   }
 
-  // `rsrc` starts at the tile's first row and ends at the matrix's last row,
-  // so rows past the matrix read as zeros; chunks past K (only in a last,
-  // partial stage) are sent out of range and read as zeros too.
+  // Stage whose first K byte (within each row) is byte0.  `rsrc` starts at
+  // the tile's first row and ends at the matrix's last row, so rows past the
+  // matrix read as zeros; chunks past K are sent out of range (zeros too).
   __device__ __forceinline__ void load(uint8_t* lds_tile, __amdgpu_buffer_rsrc_t rsrc,
                                        uint32_t row_bytes, uint32_t byte0, int wave) const {
-    const bool in_k = byte0 + chunk16 < row_bytes;
 #pragma unroll
-    for (int j = 0; j < kInstr; ++j) {
-      const int ji = wave * kInstr + j;
-      const uint32_t off = in_k ? lane_off + ji * instr_step : kOutOfRange;
+    for (int j = 0; j < S::kInstr; ++j) {
+      const int ji = wave * S::kInstr + j;
+      const int odd = ji & 1;
+      const uint32_t off =
+          byte0 + chunk16[odd] < row_bytes ? lane_off[odd] + ji * instr_step : kOutOfRange;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rsrc, (__attribute__((address_space(3))) void*)(lds_tile + ji * 1024), 16, off, byte0,
           0, 0);
@@ -201,65 +208,62 @@ struct Stager {
   }
 };
 
-// MFMA operand of row r for K sub-step ks (64 elements) of the staged tile.
+// MFMA operand of row r for K step h (0/1) of a staged tile.
 template <int ELEM>
-__device__ __forceinline__ v8i read_operand(const uint8_t* lds, int r, int ks, int g) {
+__device__ __forceinline__ v8i read_operand(const uint8_t* lds, int r, int h, int g) {
   if (ELEM == kE4M3) {
-    const v4i lo = *reinterpret_cast<const v4i*>(lds + lds_off<ELEM>(r, 4 * ks + g));
-    const v4i hi = *reinterpret_cast<const v4i*>(lds + lds_off<ELEM>(r, 4 * ks + 2 + g));
+    const v4i lo = *reinterpret_cast<const v4i*>(lds + lds_off<ELEM>(r, 4 * h + g));
+    const v4i hi = *reinterpret_cast<const v4i*>(lds + lds_off<ELEM>(r, 4 * h + 2 + g));
     return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
   } else {
-    const v4i lo = *reinterpret_cast<const v4i*>(lds + lds_off<ELEM>(r, 2 * ks + g));
+    const v4i lo = *reinterpret_cast<const v4i*>(lds + lds_off<ELEM>(r, 2 * h + g));
     return v8i{lo.x, lo.y, lo.z, lo.w, 0, 0, 0, 0};
   }
 }
 
-// The four scale bytes of blocks [kb0, kb0+4) of row r of a tile, from a
-// buffer resource over the tile's scale rows.  Bytes past the resource (rows
-// past the matrix) and blocks past K read as 0 -- a finite scale (2^-127)
-// multiplying zero codes.  DWORD: one 4-byte load (row stride and base are
-// 4-byte aligned); otherwise four byte loads.
-template <bool DWORD>
-__device__ __forceinline__ uint32_t load_scales4(__amdgpu_buffer_rsrc_t rs, int r,
-                                                 int64_t kblocks, int64_t kb0) {
-  const uint32_t base = (uint32_t)(r * kblocks + kb0);
-  if (DWORD) return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, base, 0, 0);
-  uint32_t v = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t off = kb0 + j < kblocks ? base + j : kOutOfRange;
-    v |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs, off, 0, 0) << (8 * j);
+// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector
+// memory operations are outstanding, leaving the other counters alone.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+template <int AE, int BE>
+struct Pipe {
+  // Stage buffers: as many as fit next to two scale chunks in 160 KiB.
+  static constexpr int kAB = Stage<AE>::kBytes + Stage<BE>::kBytes;
+  static constexpr int kStages = kAB <= 32768 ? 4 : 2;
+  // Stages walked per loop iteration: whole scale chunks of both parities.
+  static constexpr int kUnroll = 2 * kChunkStages;
+  static_assert(kUnroll % kStages == 0, "buffer slots must repeat within the unrolled body");
+  static constexpr int kDma = Stage<AE>::kInstr + Stage<BE>::kInstr;  // per wave and stage
+  static constexpr int kScaleDma = 2;                                  // per wave and chunk
+  // Loads a wave issues along with stage s: its code tiles, plus the scale
+  // chunk that starts with it.
+  static constexpr int ops(int s) { return kDma + (s % kChunkStages == 0 ? kScaleDma : 0); }
+  // Outstanding loads allowed when stage s starts: those of stages
+  // s+1 .. s+kStages-2 (issued earlier, kStages-1 stages ahead).
+  static constexpr int pending(int s) {
+    int n = 0;
+    for (int d = 1; d <= kStages - 2; ++d) n += ops(s + d);
+    return n;
   }
-  return v;
-}
+};
 
-template <int AE, int BE, int KS>
-__device__ __forceinline__ void mfma_substep(v16f (&acc)[4][4], const uint8_t* la,
-                                             const uint8_t* lb, int arow0, int brow0, int lr,
-                                             int g, const uint32_t (&sa)[4],
-                                             const uint32_t (&sb)[4]) {
-  v8i af[4], bf[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) af[i] = read_operand<AE>(la, arow0 + 32 * i + lr, KS, g);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) bf[j] = read_operand<BE>(lb, brow0 + 32 * j + lr, KS, g);
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          af[i], bf[j], acc[i][j], Operand<AE>::kFmt, Operand<BE>::kFmt, 2 * KS, (int)sa[i],
-          2 * KS, (int)sb[j]);
-}
-
-template <int AE, int BE, bool SDW>
+template <int AE, int BE>
 __global__ void __launch_bounds__(kTThreads)
 block_matmul_tiled(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa,
                    const uint8_t* __restrict__ b, const uint8_t* __restrict__ sb,
                    float* __restrict__ c, int64_t M, int64_t N, int64_t K, int accumulate,
                    int tiles_m, int tiles_n) {
-  constexpr int kA = Stage<AE>::kBytes, kB = Stage<BE>::kBytes;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * (kA + kB)];
+  using P = Pipe<AE, BE>;
+  constexpr int kA = Stage<AE>::kBytes, kAB = P::kAB, kStages = P::kStages;
+  // One array per buffer, always indexed by a compile-time slot, so that the
+  // compiler can tell the direct-to-LDS loads into one buffer from the reads
+  // of another and keep the loads in flight.
+  __shared__ __attribute__((aligned(1024))) uint8_t smem0[kAB];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem1[kAB];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem2[kStages > 2 ? kAB : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem3[kStages > 3 ? kAB : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t scales0[kScaleBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t scales1[kScaleBytes];
 
   // Tile order: the hardware deals workgroups round-robin to the 8 XCDs, so
   // give each XCD a contiguous range of tiles, walked in groups of up to 8
@@ -279,19 +283,22 @@ block_matmul_tiled(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave >> 1, wn = wave & 1, g = lane >> 5, lr = lane & 31;
-  const uint32_t a_row_bytes = (uint32_t)(AE == kE2M1 ? K / 2 : K);
-  const uint32_t b_row_bytes = (uint32_t)(BE == kE2M1 ? K / 2 : K);
+  const uint32_t Ku = (uint32_t)K;
+  const uint32_t a_row_bytes = AE == kE2M1 ? Ku / 2 : Ku;
+  const uint32_t b_row_bytes = BE == kE2M1 ? Ku / 2 : Ku;
   const Stager<AE> stage_a(a_row_bytes, lane);
   const Stager<BE> stage_b(b_row_bytes, lane);
-  const int64_t kblocks = K / 32;
-  const int nstages = (int)((K + kTK - 1) / kTK);
+  const uint32_t kblocks = Ku / 32;
   const int64_t rows_a = min(M - m0, (int64_t)kTM), rows_b = min(N - n0, (int64_t)kTN);
+  // (a 256-row slab of either operand is below 2^31 bytes: checked at launch)
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(a + m0 * a_row_bytes, rows_a * a_row_bytes);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(b + n0 * b_row_bytes, rows_b * b_row_bytes);
-  // (a 256-row slab of either operand is below 2^31 bytes: checked at launch)
   const __amdgpu_buffer_rsrc_t rsa = make_rsrc(sa + m0 * kblocks, rows_a * kblocks);
   const __amdgpu_buffer_rsrc_t rsb = make_rsrc(sb + n0 * kblocks, rows_b * kblocks);
   const int ar = wm * 128 + lr, br = wn * 128 + lr;  // this lane's first A / B^T tile row
+  // Scale staging: wave w fetches rows [64w, 64w+64) of A and of B^T, one
+  // 16-byte row slice per lane (blocks [16 * chunk, 16 * chunk + 16)).
+  const uint32_t scale_lane_off = (uint32_t)(64 * wave + lane) * kblocks;
 
   v16f acc[4][4];
 #pragma unroll
@@ -301,53 +308,106 @@ block_matmul_tiled(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  uint32_t sac[4], sbc[4], san[4], sbn[4];
-  stage_a.load(smem, ra, a_row_bytes, 0, wave);
-  stage_b.load(smem + kA, rb, b_row_bytes, 0, wave);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    san[i] = load_scales4<SDW>(rsa, ar + 32 * i, kblocks, 0);
-    sbn[i] = load_scales4<SDW>(rsb, br + 32 * i, kblocks, 0);
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  auto slot = [&](int buf) -> uint8_t* {
+    return buf == 0 ? smem0 : buf == 1 ? smem1 : buf == 2 ? smem2 : smem3;
+  };
+  // Issue stage st into buffer (st % kStages); the first stage of a scale
+  // chunk also fetches the chunk's scales into the set of the chunk's parity.
+  auto issue = [&](int st, int buf, int par) {
+    uint8_t* dst = slot(buf);
+    stage_a.load(dst, ra, a_row_bytes, (uint32_t)st * Stage<AE>::kRowBytes, wave);
+    stage_b.load(dst + kA, rb, b_row_bytes, (uint32_t)st * Stage<BE>::kRowBytes, wave);
+    if (st % kChunkStages == 0) {
+      const uint32_t kb = (uint32_t)(st / kChunkStages) * kScaleRowBytes;
+      const uint32_t off = kb < kblocks ? scale_lane_off : kOutOfRange;
+      uint8_t* sdst = (par ? scales1 : scales0) + wave * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsa, (__attribute__((address_space(3))) void*)sdst, 16, off, kb, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsb, (__attribute__((address_space(3))) void*)(sdst + kScaleBytes / 2), 16, off, kb, 0,
+          0);
+    }
+  };
 
-  for (int st = 0; st < nstages; ++st) {
-    // Scales of this stage, shifted so that byte 0 / byte 2 hold this lane's
-    // block of K sub-step 0 / 1 (lane group g takes block g of each sub-step).
+  // The stage count is padded to whole loop iterations (kUnroll stages, 1024
+  // K elements); stages past K load out of range (zero codes, zero scale
+  // bytes) and add nothing.  Prologue: stages 0 .. kStages-2 in flight.
+  const int iters = (int)((Ku + P::kUnroll * kTK - 1) / (P::kUnroll * kTK));
+#pragma unroll
+  for (int u = 0; u < kStages - 1; ++u) issue(u, u, 0);
+
+  int it = 0;
+  auto stage = [&](auto U) {
+    constexpr int u = decltype(U)::value;
+    constexpr int buf = u % kStages, par = u / kChunkStages % 2, sub = u % kChunkStages;
+    constexpr int nu = u + kStages - 1;  // stage issued now, relative to the iteration
+    const int st = it * P::kUnroll + u;
+    // Wait for this stage's loads (later stages stay in flight), then make
+    // them visible to every wave.  A bare s_barrier: a fenced __syncthreads
+    // would also drain the later stages' loads.  The barrier also certifies
+    // that every wave has consumed (in its MFMAs) its reads of the buffer the
+    // issue below overwrites.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(P::pending(u)));
+    __builtin_amdgcn_s_barrier();
+    issue(st + kStages - 1, nu % kStages, nu / kChunkStages % 2);
+
+    const uint8_t* la = slot(buf);
+    const uint8_t* lb = la + kA;
+    const uint8_t* sc = par ? scales1 : scales0;
+    // Scale dword of this stage (blocks [4 sub, 4 sub + 4) of the chunk) of
+    // each row, shifted so that byte 0 / byte 2 hold this lane's block of
+    // K step 0 / 1 (lane group g takes block g of each step).
+    int sas[4], sbs[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      sac[i] = san[i] >> (8 * g);
-      sbc[i] = sbn[i] >> (8 * g);
+      sas[i] = (int)(*reinterpret_cast<const uint32_t*>(sc + (ar + 32 * i) * kScaleRowBytes +
+                                                        4 * sub) >> (8 * g));
+      sbs[i] = (int)(*reinterpret_cast<const uint32_t*>(sc + kScaleBytes / 2 +
+                                                        (br + 32 * i) * kScaleRowBytes +
+                                                        4 * sub) >> (8 * g));
     }
-    const uint8_t* cur = smem + (st & 1) * (kA + kB);
-    uint8_t* nxt = smem + ((st + 1) & 1) * (kA + kB);
-    if (st + 1 < nstages) {
-      stage_a.load(nxt, ra, a_row_bytes, (uint32_t)(st + 1) * Stage<AE>::kRowBytes, wave);
-      stage_b.load(nxt + kA, rb, b_row_bytes, (uint32_t)(st + 1) * Stage<BE>::kRowBytes, wave);
+    auto kstep = [&](auto H) {
+      constexpr int h = decltype(H)::value;
+      v8i af[4], bf[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        san[i] = load_scales4<SDW>(rsa, ar + 32 * i, kblocks, 4 * (st + 1));
-        sbn[i] = load_scales4<SDW>(rsb, br + 32 * i, kblocks, 4 * (st + 1));
-      }
-    }
-    mfma_substep<AE, BE, 0>(acc, cur, cur + kA, wm * 128, wn * 128, lr, g, sac, sbc);
-    mfma_substep<AE, BE, 1>(acc, cur, cur + kA, wm * 128, wn * 128, lr, g, sac, sbc);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+      for (int i = 0; i < 4; ++i) af[i] = read_operand<AE>(la, ar + 32 * i, h, g);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) bf[q] = read_operand<BE>(lb, br + 32 * q, h, g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          acc[i][q] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              af[i], bf[q], acc[i][q], Operand<AE>::kFmt, Operand<BE>::kFmt, 2 * h, sas[i],
+              2 * h, sbs[q]);
+    };
+    kstep(std::integral_constant<int, 0>{});
+    kstep(std::integral_constant<int, 1>{});
+  };
+  for (; it < iters; ++it) {
+    stage(std::integral_constant<int, 0>{});
+    stage(std::integral_constant<int, 1>{});
+    stage(std::integral_constant<int, 2>{});
+    stage(std::integral_constant<int, 3>{});
+    stage(std::integral_constant<int, 4>{});
+    stage(std::integral_constant<int, 5>{});
+    stage(std::integral_constant<int, 6>{});
+    stage(std::integral_constant<int, 7>{});
   }
+  // No load may still be writing this workgroup's LDS when it exits.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
   // Epilogue: lane holds C[8(e/4) + 4g + (e%4)][lr] of each 32x32 tile.
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t col = n0 + wn * 128 + 32 * j + lr;
+    for (int q = 0; q < 4; ++q) {
+      const int64_t col = n0 + wn * 128 + 32 * q + lr;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int64_t row = m0 + wm * 128 + 32 * i + 8 * (e >> 2) + 4 * g + (e & 3);
         if (row < M && col < N) {
-          float v = acc[i][j][e];
+          float v = acc[i][q][e];
           if (accumulate) v += c[row * N + col];
           c[row * N + col] = v;
         }
@@ -360,16 +420,9 @@ hipError_t launch_tiled(const uint8_t* a, const uint8_t* sa, const uint8_t* b, c
                         float* c, int64_t M, int64_t N, int64_t K, int accumulate,
                         hipStream_t stream) {
   const int64_t tiles_m = (M + kTM - 1) / kTM, tiles_n = (N + kTN - 1) / kTN;
-  const int64_t kblocks = K / 32;
-  const bool dw = (kblocks % 4 == 0) && ((reinterpret_cast<uintptr_t>(sa) & 3) == 0) &&
-                  ((reinterpret_cast<uintptr_t>(sb) & 3) == 0);
-  const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kTThreads);
-  if (dw)
-    hipLaunchKernelGGL((block_matmul_tiled<AE, BE, true>), grid, block, 0, stream, a, sa, b, sb,
-                       c, M, N, K, accumulate, (int)tiles_m, (int)tiles_n);
-  else
-    hipLaunchKernelGGL((block_matmul_tiled<AE, BE, false>), grid, block, 0, stream, a, sa, b,
-                       sb, c, M, N, K, accumulate, (int)tiles_m, (int)tiles_n);
+  hipLaunchKernelGGL((block_matmul_tiled<AE, BE>), dim3((unsigned)(tiles_m * tiles_n)),
+                     dim3(kTThreads), 0, stream, a, sa, b, sb, c, M, N, K, accumulate,
+                     (int)tiles_m, (int)tiles_n);
   return hipGetLastError();
 }
 
@@ -378,9 +431,13 @@ hipError_t launch_typed(const uint8_t* a, const uint8_t* sa, const uint8_t* b,
                         const uint8_t* sb, float* c, int64_t M, int64_t N, int64_t K,
                         int accumulate, hipStream_t stream) {
   // The tiled kernel addresses a 256-row slab of either operand with 32-bit
-  // buffer offsets.
+  // buffer offsets, and stages scales as aligned 16-byte row slices (16
+  // blocks), so it needs K % 512 == 0 and 16-byte aligned scale arrays.
   const int64_t slab_a = 256 * (AE == kE2M1 ? K / 2 : K), slab_b = 256 * (BE == kE2M1 ? K / 2 : K);
-  if (M > 64 && slab_a < (1ll << 31) && slab_b < (1ll << 31))
+  const bool scale_slices = (K % 512 == 0) && ((reinterpret_cast<uintptr_t>(sa) & 15) == 0) &&
+                            ((reinterpret_cast<uintptr_t>(sb) & 15) == 0);
+  if (M > 64 && scale_slices && slab_a < (1ll << 31) && slab_b < (1ll << 31) &&
+      M * (K / 32) < (1ll << 31) && N * (K / 32) < (1ll << 31))
     return launch_tiled<AE, BE>(a, sa, b, sb, c, M, N, K, accumulate, stream);
   const int64_t tiles = ((M + 15) / 16) * ((N + 15) / 16);
   const int64_t grid = (tiles + 3) / 4;

@@ -44,8 +44,11 @@ def rand_operand(rng, rows, K, elem, lo=112, hi=142, nan_codes=False):
     return codes, rng.integers(lo, hi, (rows, K // 32), dtype=np.uint8)
 
 
+# Small and decode-like shapes, K not a multiple of 128, and shapes for the
+# 256x256-tile kernel with partial tiles in M and N and partial K groups.
 SHAPES = [(1, 1, 32), (3, 4, 96), (16, 16, 128), (17, 33, 160), (64, 48, 1024),
-          (100, 70, 3968), (256, 256, 512), (300, 257, 2080)]
+          (100, 70, 3968), (256, 256, 512), (300, 257, 2080), (257, 300, 1152),
+          (130, 520, 640), (512, 256, 128)]
 
 
 def quantized_normal(rng, rows, K, elem, sigma=1.0, outliers=0.01, factor=30.0):
@@ -108,7 +111,7 @@ def test_random_codes_mfma_bound(ae, be, M, N, K):
 @pytest.mark.parametrize("ae,be", PAIRS)
 def test_accumulate(ae, be):
     rng = np.random.default_rng(77)
-    M, N, K = 40, 72, 384
+    M, N, K = 140, 72, 384
     ac, asc = quantized_normal(rng, M, K, ae)
     bc, bsc = quantized_normal(rng, N, K, be)
     cin = (rng.standard_normal((M, N)) * 1e7).astype(np.float32)
