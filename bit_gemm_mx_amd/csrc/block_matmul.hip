@@ -383,6 +383,18 @@ block_matmul_tiled(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa
     };
     kstep(std::integral_constant<int, 0>{});
     kstep(std::integral_constant<int, 1>{});
+    // Instruction order for the scheduler: the operand and scale reads of the
+    // first K step, then one MFMA, one global load and one LDS read at a
+    // time, so that the loads of the next stage drain through the memory
+    // pipeline while the MFMAs run instead of stalling the wave in a burst.
+    constexpr int kMfma = 32, kVmem = P::kDma + (nu % kChunkStages == 0 ? P::kScaleDma : 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);  // LDS reads
+#pragma unroll
+    for (int k = 0; k < kMfma; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
+      if (k < kVmem) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);              // LDS read
+    }
   };
   for (; it < iters; ++it) {
     stage(std::integral_constant<int, 0>{});
