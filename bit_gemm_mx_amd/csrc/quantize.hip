@@ -11,11 +11,23 @@
 //     wave's load instruction reads 1 KiB of contiguous memory;
 //   * each lane keeps kUnroll loads in flight (4 KiB per wave per iteration);
 //   * amax is an integer max over |x| bit patterns (exact, and any NaN/Inf
-//     compares above every finite value) reduced over the 8 lanes with DPP;
-//   * rounding is done on the bit pattern of y: adding (half step - 1) and
-//     truncating the mantissa is round-to-nearest with ties down, valid in
-//     the normal binades of the element format; the subnormal range (uniform
-//     spacing) uses ceil(y/spacing - 1/2), which also rounds ties down.
+//     compares above every finite value) reduced over the 8 lanes with DPP.
+//
+// Rounding, fast path: gfx950's v_cvt_scalef32_pk_{fp4,fp8}_f32 compute the
+// round-to-nearest-even code of x / s for a float scale s (checked on the
+// hardware for every normal power-of-two scale), saturating for FP4 and
+// overflowing to NaN for FP8 (so |x| is clamped to 448 * 2^e first).  Nearest
+// with ties to the smaller magnitude differs from nearest-even only at exact
+// midpoints, and a midpoint has at most 2 (E2M1) / 4 (E4M3) significant bits:
+// its 21 / 19 low mantissa bits are zero.  -0.0 has them zero too.  So a wave
+// takes the fast path unless one of its elements has those bits zero (or its
+// block's scale is near the bottom of the range, where f32 subnormals and a
+// subnormal scale appear); random data essentially never leaves it.
+//
+// Rounding, exact path: on the bit pattern of y, adding (half step - 1) and
+// truncating the mantissa is round-to-nearest with ties down in the normal
+// binades of the element format; the subnormal range (uniform spacing) uses
+// ceil(y / spacing - 1/2), which also rounds ties down.
 #include "mx_internal.h"
 
 namespace mx {
@@ -39,6 +51,7 @@ struct Fmt<kE2M1> {
   static constexpr uint32_t kCodeOffset = 252u;        // (127 - 1) << 1: q(1.0) - code(1.0)
   static constexpr uint32_t kTopQ = 259u;              // q of 6.0
   static constexpr float kInvSpacing = 2.0f;           // subnormal spacing 0.5
+  static constexpr int kTieShift = 11;                 // keeps the 21 low mantissa bits
 };
 
 // E4M3 (f8E4M3FN): normal binades start at 2^-6, top finite value 448.
@@ -52,6 +65,7 @@ struct Fmt<kE4M3> {
   static constexpr uint32_t kCodeOffset = 960u;        // (127 - 7) << 3
   static constexpr uint32_t kTopQ = 1086u;             // q of 448 (code 0x7E)
   static constexpr float kInvSpacing = 512.0f;         // subnormal spacing 2^-9
+  static constexpr int kTieShift = 13;                 // keeps the 19 low mantissa bits
 };
 
 // Max of v over each aligned group of 8 lanes.
@@ -81,6 +95,40 @@ __device__ __forceinline__ uint32_t element_code(uint32_t xb, float inv_scale) {
   return magnitude_index<ELEM>(y) | neg;
 }
 
+typedef short v2s __attribute__((ext_vector_type(2)));
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+// Codes of 4 elements by the hardware convert (fast path): E2M1 -> 16 bits,
+// E4M3 -> 32 bits, element 0 lowest.
+template <int ELEM>
+__device__ __forceinline__ uint32_t convert4(float4 v, float scale, float clamp) {
+  if (ELEM == kE2M1) {
+    uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v.x, v.y, scale, 0);
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v.z, v.w, scale, 1);
+  } else {
+    // FP8 conversion overflows to NaN past 464 * scale: clamp to the grid top.
+    const float x0 = __builtin_amdgcn_fmed3f(v.x, -clamp, clamp);
+    const float x1 = __builtin_amdgcn_fmed3f(v.y, -clamp, clamp);
+    const float x2 = __builtin_amdgcn_fmed3f(v.z, -clamp, clamp);
+    const float x3 = __builtin_amdgcn_fmed3f(v.w, -clamp, clamp);
+    v2s w = {0, 0};
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, x0, x1, scale, false);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(w, x2, x3, scale, true);
+    return (uint32_t)(uint16_t)w[0] | ((uint32_t)(uint16_t)w[1] << 16);
+  }
+}
+
+// Codes of 4 elements by exact integer rounding (exact path).
+template <int ELEM>
+__device__ __forceinline__ uint32_t round4(float4 v, float inv_scale) {
+  const uint32_t c0 = element_code<ELEM>(__float_as_uint(v.x), inv_scale);
+  const uint32_t c1 = element_code<ELEM>(__float_as_uint(v.y), inv_scale);
+  const uint32_t c2 = element_code<ELEM>(__float_as_uint(v.z), inv_scale);
+  const uint32_t c3 = element_code<ELEM>(__float_as_uint(v.w), inv_scale);
+  return ELEM == kE2M1 ? c0 | (c1 << 4) | (c2 << 8) | (c3 << 12)
+                       : c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+}
+
 template <int ELEM>
 __global__ void __launch_bounds__(kThreads)
 quantize_kernel(const float4* __restrict__ x, uint8_t* __restrict__ codes,
@@ -98,39 +146,75 @@ quantize_kernel(const float4* __restrict__ x, uint8_t* __restrict__ codes,
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int64_t blk = blk0 + 8 * u;
-      v[u] = blk < n_blocks ? x[blk * 8 + sub] : make_float4(0.f, 0.f, 0.f, 0.f);
+      if (blk < n_blocks) {
+        // Each input byte is read once: a non-temporal load does not displace
+        // useful cache lines.
+        const f4v t = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(&x[blk * 8 + sub]));
+        v[u] = make_float4(t[0], t[1], t[2], t[3]);
+      } else {
+        v[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
     }
+    uint32_t amax[kUnroll];
+    uint32_t low = 0xFFFFFFFFu;  // min over elements of their low mantissa bits
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int64_t blk = blk0 + 8 * u;
       const uint32_t b0 = __float_as_uint(v[u].x), b1 = __float_as_uint(v[u].y);
       const uint32_t b2 = __float_as_uint(v[u].z), b3 = __float_as_uint(v[u].w);
-      uint32_t amax = max(max(b0 & 0x7FFFFFFFu, b1 & 0x7FFFFFFFu),
-                          max(b2 & 0x7FFFFFFFu, b3 & 0x7FFFFFFFu));
-      amax = max_over_8_lanes(amax);
+      amax[u] = max(max(b0 & 0x7FFFFFFFu, b1 & 0x7FFFFFFFu), max(b2 & 0x7FFFFFFFu, b3 & 0x7FFFFFFFu));
+      low = min(low, min(min(b0 << F::kTieShift, b1 << F::kTieShift),
+                         min(b2 << F::kTieShift, b3 << F::kTieShift)));
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) amax[u] = max_over_8_lanes(amax[u]);
 
+    float inv_scale[kUnroll], scale[kUnroll];
+    uint32_t byte[kUnroll];
+    bool nonfinite[kUnroll];
+    bool exact = low == 0;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
       // floor(log2 amax) from the bit pattern (subnormals via the leading bit).
-      const int fl = amax >= 0x00800000u ? (int)(amax >> 23) - 127 : (31 - (int)__clz(amax)) - 149;
+      const uint32_t a = amax[u];
+      const int fl = a >= 0x00800000u ? (int)(a >> 23) - 127 : (31 - (int)__clz(a)) - 149;
       const int e = min(max(fl - F::kEmax, -127), 127);
-      const float inv_scale = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, normal
-      const bool nonfinite = amax >= 0x7F800000u;
-      uint32_t byte = amax == 0 ? 127u : (nonfinite ? 0xFFu : (uint32_t)(e + 127));
+      inv_scale[u] = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, normal
+      nonfinite[u] = a >= 0x7F800000u;
+      byte[u] = a == 0 ? 127u : (nonfinite[u] ? 0xFFu : (uint32_t)(e + 127));
+      // 2^e itself, for the convert; blocks below amax 2^-100 (and all-zero
+      // blocks) take the exact path.
+      scale[u] = __uint_as_float((uint32_t)max(e + 127, 1) << 23);
+      exact |= a < 0x0D800000u;
+    }
 
-      const uint32_t c0 = element_code<ELEM>(b0, inv_scale);
-      const uint32_t c1 = element_code<ELEM>(b1, inv_scale);
-      const uint32_t c2 = element_code<ELEM>(b2, inv_scale);
-      const uint32_t c3 = element_code<ELEM>(b3, inv_scale);
-      if (blk < n_blocks) {
-        if (ELEM == kE2M1) {
-          uint32_t w = c0 | (c1 << 4) | (c2 << 8) | (c3 << 12);
-          w = nonfinite ? 0u : w;
-          reinterpret_cast<uint16_t*>(codes)[blk * 8 + sub] = (uint16_t)w;
-        } else {
-          uint32_t w = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
-          w = nonfinite ? 0u : w;
-          reinterpret_cast<uint32_t*>(codes)[blk * 8 + sub] = w;
+    if (__ballot(exact) == 0) {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t blk = blk0 + 8 * u;
+        const float top = ELEM == kE4M3 ? 448.0f * scale[u] : 0.0f;
+        uint32_t w = convert4<ELEM>(v[u], scale[u], top);
+        w = nonfinite[u] ? 0u : w;
+        if (blk < n_blocks) {
+          if (ELEM == kE2M1)
+            reinterpret_cast<uint16_t*>(codes)[blk * 8 + sub] = (uint16_t)w;
+          else
+            reinterpret_cast<uint32_t*>(codes)[blk * 8 + sub] = w;
+          if (sub == 0) scales[blk] = (uint8_t)byte[u];
         }
-        if (sub == 0) scales[blk] = (uint8_t)byte;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int64_t blk = blk0 + 8 * u;
+        uint32_t w = round4<ELEM>(v[u], inv_scale[u]);
+        w = nonfinite[u] ? 0u : w;
+        if (blk < n_blocks) {
+          if (ELEM == kE2M1)
+            reinterpret_cast<uint16_t*>(codes)[blk * 8 + sub] = (uint16_t)w;
+          else
+            reinterpret_cast<uint32_t*>(codes)[blk * 8 + sub] = w;
+          if (sub == 0) scales[blk] = (uint8_t)byte[u];
+        }
       }
     }
   }
@@ -140,9 +224,9 @@ int grid_for(int64_t n_blocks) {
   const int64_t iters = (n_blocks + kBlocksPerWaveIter - 1) / kBlocksPerWaveIter;
   const int64_t waves_per_wg = kThreads / 64;
   int64_t wgs = (iters + waves_per_wg - 1) / waves_per_wg;
-  // Enough workgroups to fill 256 CUs several times over; the grid-stride
-  // loop covers the rest.
-  const int64_t cap = 256 * 16;
+  // Enough workgroups to fill 256 CUs many times over (measured best for the
+  // 8192x8192 stream); the grid-stride loop covers the rest.
+  const int64_t cap = 256 * 64;
   return (int)(wgs < cap ? wgs : cap);
 }
 
