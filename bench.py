@@ -121,14 +121,25 @@ def bench_codec(mx, W, torch, steps, warmup):
         step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # A second pass over the same steps with per-kernel events.
+    # Per-kernel durations: each kernel alone, `steps` back-to-back launches
+    # (rotating over the copies) between one pair of HIP events on the stream
+    # the kernels run on, so that the event overhead is not charged per launch.
     timer = EventTimer(torch)
-    for i in range(steps):
-        step(i, timer)
+
+    def q_only():
+        for i in range(steps):
+            mx.quantize(xs[i % copies], mx.MX_E2M1, out=qs[i % copies])
+
+    def d_only():
+        for i in range(steps):
+            mx.dequantize(qs[i % copies], out=ys[i % copies])
+
+    timer.run("quantize", q_only)
+    timer.run("dequantize", d_only)
     torch.cuda.synchronize()
     per_op = codec_bytes(rows, cols, 0.5)
-    q_ms, q_min = timer.mean_ms("quantize")
-    d_ms, d_min = timer.mean_ms("dequantize")
+    q_ms, q_min = (v / steps for v in timer.mean_ms("quantize"))
+    d_ms, d_min = (v / steps for v in timer.mean_ms("dequantize"))
     kernels = {
         "quantize_e2m1": dict(ms=q_ms, min_ms=q_min, bytes=per_op, src="quantize.hip",
                               kernel="quantize_kernel<1>"),
@@ -156,14 +167,22 @@ def bench_matmuls(mx, W, torch, reps):
     out = {}
 
     def timed(name, fn, n):
+        """Average duration of fn over n back-to-back calls between one pair of
+        HIP events (and the fastest of three such groups)."""
         for _ in range(2):
             fn()
         torch.cuda.synchronize()
         t = EventTimer(torch)
-        for _ in range(n):
-            t.run(name, fn)
+
+        def group():
+            for _ in range(n):
+                fn()
+
+        for _ in range(3):
+            t.run(name, group)
         torch.cuda.synchronize()
-        return t.mean_ms(name)
+        mean, best = t.mean_ms(name)
+        return mean / n, best / n
 
     # decode-shaped MXFP4 x MXFP4
     a, bt = W.decode_matmul_case()
@@ -258,6 +277,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-matmul", action="store_true", help="time the codec step only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-codec", action="store_true",
+                    help="skip the codec step (profiling the matmul workloads alone)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device-to-device copy, the reference that "
+                         "scales the FETCH_SIZE / WRITE_SIZE counters of a --pmc run")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the MX hot path has no "
@@ -276,6 +300,17 @@ def main():
         raise RuntimeError("no GPU visible: bench.py measures the HIP path only")
     torch.cuda.set_device(0)
 
+    if args.copy_calibration:
+        src = torch.empty(64 * 1024 * 1024, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    if args.no_codec:
+        parts = bench_matmuls(mx, W, torch, max(3, args.steps // 2))
+        print(json.dumps({"metric": METRIC, "parts": parts, "note": "matmul workloads only"}))
+        return
     progress("codec step: quantize + dequantize of the 8192x8192 weight workload")
     wall, step_bytes, kernels = bench_codec(mx, W, torch, args.steps, args.warmup)
     progress(f"codec step done: {wall / args.steps * 1e3:.3f} ms/step")
