@@ -73,41 +73,165 @@ __device__ __forceinline__ int load_scale(const uint8_t* scales, int64_t row, in
   return (row < rows && kb < kblocks) ? (int)scales[row * kblocks + kb] : 127;
 }
 
-// One wave computes one 16x16 tile of C.
-template <int AE, int BE>
-__global__ void __launch_bounds__(256)
-block_matmul_simple(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa,
-                    const uint8_t* __restrict__ b, const uint8_t* __restrict__ sb,
-                    float* __restrict__ c, int64_t M, int64_t N, int64_t K, int accumulate) {
-  const int lane = threadIdx.x & 63;
-  const int64_t tile = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
-  const int64_t tiles_n = (N + 15) / 16;
-  const int64_t tiles = ((M + 15) / 16) * tiles_n;
-  if (tile >= tiles) return;
-  const int64_t m0 = (tile / tiles_n) * 16, n0 = (tile % tiles_n) * 16;
-  const int64_t kblocks = K / 32;
-  const int64_t arow = m0 + (lane & 15), brow = n0 + (lane & 15);
-  const int kq = lane >> 4;
+// ---------------------------------------------------------------------------
+// Skinny kernel, for few rows of A (token-by-token decode) and for the shapes
+// the tiled kernel does not take.  Such a product streams B once and is bound
+// by how fast B arrives, so the design goal is many loads in flight early,
+// each touching as few cache lines as possible:
+//   * a workgroup of 8 waves owns 16 columns of C and up to 64 rows (T tiles
+//     of the 16x16x128 scaled MFMA); its waves split K into 8 contiguous
+//     ranges, each wave issues the loads of U K steps at once and then runs
+//     their MFMAs, and the 8 partial tiles are summed in LDS in a fixed order
+//     (so results are reproducible bit for bit);
+//   * loads use a "quad" layout -- lane 4r + q fetches 16-byte chunk q of
+//     row r, so each group of four lanes reads one contiguous 64-byte piece
+//     -- and a cross-lane permute (ds_bpermute) moves the chunks into the
+//     MFMA layout (lane 16g + r holds chunk g of row r).  Loading in the MFMA
+//     layout directly would have every four lanes touch four rows;
+//   * scale bytes travel the same way, one dword (one K step's four blocks)
+//     per lane when rows of scales are dword aligned.
+// Each B^T row slice is loaded once and used for all T row tiles of A.
+// ---------------------------------------------------------------------------
+constexpr int kSkinnyWaves = 8;
+constexpr int kSkinnyThreads = 64 * kSkinnyWaves;
 
-  v4f acc = {0.f, 0.f, 0.f, 0.f};
-  for (int64_t kb0 = 0; kb0 < kblocks; kb0 += 4) {
-    const int64_t kb = kb0 + kq;
-    const v8i av = load_operand<AE>(a, arow, M, kb0 * 32, kq, K);
-    const v8i bv = load_operand<BE>(b, brow, N, kb0 * 32, kq, K);
-    const int as = load_scale(sa, arow, M, kb, kblocks);
-    const int bs = load_scale(sb, brow, N, kb, kblocks);
-    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, Operand<AE>::kFmt,
-                                                           Operand<BE>::kFmt, 0, as, 0, bs);
-  }
-  const int64_t col = n0 + (lane & 15);
+// Lane-permute one dword: every lane receives `v` of lane `addr / 4`.
+__device__ __forceinline__ int lane_fetch(int addr, int v) {
+  return __builtin_amdgcn_ds_bpermute(addr, v);
+}
+
+template <int ELEM>
+__device__ __forceinline__ v8i to_mfma_layout(v8i v, int addr) {
+  v8i r;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t row = m0 + 4 * kq + j;
-    if (row < M && col < N) {
-      float v = acc[j];
-      if (accumulate) v += c[row * N + col];
-      c[row * N + col] = v;
+  for (int i = 0; i < 8; ++i) r[i] = (ELEM == kE2M1 && i >= 4) ? 0 : lane_fetch(addr, v[i]);
+  return r;
+}
+
+// Scale dword of K step s of row `row` (its four blocks), or 127s outside.
+__device__ __forceinline__ int load_scale_dword(const uint8_t* scales, int64_t row, int64_t rows,
+                                                int64_t s, int64_t kblocks) {
+  return row < rows ? (int)*reinterpret_cast<const uint32_t*>(scales + row * kblocks + 4 * s)
+                    : 0x7F7F7F7F;
+}
+
+template <int AE, int BE, int T>
+__global__ void __launch_bounds__(kSkinnyThreads)
+block_matmul_skinny(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa,
+                    const uint8_t* __restrict__ b, const uint8_t* __restrict__ sb,
+                    float* __restrict__ c, int64_t M, int64_t N, int64_t K, int accumulate,
+                    int scale_dwords) {
+  // K steps per load batch: fewer when many row tiles share the registers.
+  constexpr int U = T >= 4 ? 2 : 4;
+  __shared__ v4f red[kSkinnyWaves][T][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int qr = lane >> 2, q = lane & 3;            // load layout: row qr, chunk q
+  const int to_mfma = 4 * (4 * (lane & 15) + (lane >> 4));  // source lane (x4) of my MFMA slot
+  const int gshift = 8 * (lane >> 4);                // my block within a step's scale dword
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int64_t kblocks = K / 32;
+  const int64_t steps = (kblocks + 3) / 4;  // 128-element MFMA K steps
+  const int64_t per_wave = (steps + kSkinnyWaves - 1) / kSkinnyWaves;
+  const int64_t s_begin = wave * per_wave;
+  const int64_t s_end = min(steps, s_begin + per_wave);
+  const int64_t brow = n0 + qr;
+
+  for (int64_t m0 = (int64_t)blockIdx.y * 16 * T; m0 < M; m0 += (int64_t)gridDim.y * 16 * T) {
+    v4f acc[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int64_t s0 = s_begin; s0 < s_end; s0 += U) {
+      // Scale loads first (in-order load counters: their permutes then only
+      // wait for them), then the operand loads, then permutes and MFMAs.
+      // Dword path (kblocks % 4 == 0, aligned): lane 4r + q holds the four
+      // blocks of step s0 + q.  Byte path: lane 4r + q holds block q of each
+      // step.
+      int bsr[U], asr[U][T];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        bsr[u] = 0x7F7F7F7F;
+#pragma unroll
+        for (int t = 0; t < T; ++t) asr[u][t] = 0x7F7F7F7F;
+      }
+      if (scale_dwords) {
+        if (q < U && s0 + q < s_end) {
+          bsr[0] = load_scale_dword(sb, brow, N, s0 + q, kblocks);
+#pragma unroll
+          for (int t = 0; t < T; ++t)
+            asr[0][t] = load_scale_dword(sa, m0 + 16 * t + qr, M, s0 + q, kblocks);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (s0 + u < s_end) {
+            const int64_t kb = 4 * (s0 + u) + q;
+            bsr[u] = load_scale(sb, brow, N, kb, kblocks);
+#pragma unroll
+            for (int t = 0; t < T; ++t) asr[u][t] = load_scale(sa, m0 + 16 * t + qr, M, kb, kblocks);
+          }
+        }
+      }
+      v8i bv[U], av[U][T];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        bv[u] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int t = 0; t < T; ++t) av[u][t] = bv[u];
+        if (s0 + u < s_end) {  // wave-uniform
+          bv[u] = load_operand<BE>(b, brow, N, 128 * (s0 + u), q, K);
+#pragma unroll
+          for (int t = 0; t < T; ++t)
+            av[u][t] = load_operand<AE>(a, m0 + 16 * t + qr, M, 128 * (s0 + u), q, K);
+        }
+      }
+      int bs[U], as[U][T];
+      if (scale_dwords) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int from = 4 * (4 * (lane & 15) + u);
+          bs[u] = lane_fetch(from, bsr[0]) >> gshift;
+#pragma unroll
+          for (int t = 0; t < T; ++t) as[u][t] = lane_fetch(from, asr[0][t]) >> gshift;
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          bs[u] = lane_fetch(to_mfma, bsr[u]);
+#pragma unroll
+          for (int t = 0; t < T; ++t) as[u][t] = lane_fetch(to_mfma, asr[u][t]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (s0 + u < s_end) {
+          const v8i bm = to_mfma_layout<BE>(bv[u], to_mfma);
+#pragma unroll
+          for (int t = 0; t < T; ++t)
+            acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                to_mfma_layout<AE>(av[u][t], to_mfma), bm, acc[t], Operand<AE>::kFmt,
+                Operand<BE>::kFmt, 0, as[u][t], 0, bs[u]);
+        }
+      }
     }
+#pragma unroll
+    for (int t = 0; t < T; ++t) red[wave][t][lane] = acc[t];
+    __syncthreads();
+    // Output o = (tile, row in tile, column): consecutive threads write
+    // consecutive columns.  Lane l of a tile holds C[4(l/16) + j][l % 16].
+    for (int o = threadIdx.x; o < T * 256; o += kSkinnyThreads) {
+      const int t = o >> 8, rr = (o >> 4) & 15, cc = o & 15;
+      const int src = 16 * (rr >> 2) + cc, j = rr & 3;
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < kSkinnyWaves; ++w) v += red[w][t][src][j];
+      const int64_t row = m0 + 16 * t + rr, col = n0 + cc;
+      if (row < M && col < N) {
+        if (accumulate) v += c[row * N + col];
+        c[row * N + col] = v;
+      }
+    }
+    __syncthreads();  // red is rewritten by the next row panel
   }
 }
 
@@ -439,6 +563,31 @@ hipError_t launch_tiled(const uint8_t* a, const uint8_t* sa, const uint8_t* b, c
 }
 
 template <int AE, int BE>
+hipError_t launch_skinny(const uint8_t* a, const uint8_t* sa, const uint8_t* b,
+                         const uint8_t* sb, float* c, int64_t M, int64_t N, int64_t K,
+                         int accumulate, hipStream_t stream) {
+  const int64_t gx = (N + 15) / 16;
+  if (gx > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const int t = M <= 16 ? 1 : M <= 32 ? 2 : 4;
+  const int64_t panels = (M + 16 * t - 1) / (16 * t);
+  const dim3 grid((unsigned)gx, (unsigned)(panels < 65535 ? panels : 65535));
+  // Scale rows can be read a dword (one K step) at a time when every row
+  // starts on a dword boundary and holds whole steps.
+  const int dw = (K % 128 == 0) && ((reinterpret_cast<uintptr_t>(sa) & 3) == 0) &&
+                 ((reinterpret_cast<uintptr_t>(sb) & 3) == 0);
+  if (t == 1)
+    hipLaunchKernelGGL((block_matmul_skinny<AE, BE, 1>), grid, dim3(kSkinnyThreads), 0, stream,
+                       a, sa, b, sb, c, M, N, K, accumulate, dw);
+  else if (t == 2)
+    hipLaunchKernelGGL((block_matmul_skinny<AE, BE, 2>), grid, dim3(kSkinnyThreads), 0, stream,
+                       a, sa, b, sb, c, M, N, K, accumulate, dw);
+  else
+    hipLaunchKernelGGL((block_matmul_skinny<AE, BE, 4>), grid, dim3(kSkinnyThreads), 0, stream,
+                       a, sa, b, sb, c, M, N, K, accumulate, dw);
+  return hipGetLastError();
+}
+
+template <int AE, int BE>
 hipError_t launch_typed(const uint8_t* a, const uint8_t* sa, const uint8_t* b,
                         const uint8_t* sb, float* c, int64_t M, int64_t N, int64_t K,
                         int accumulate, hipStream_t stream) {
@@ -451,11 +600,7 @@ hipError_t launch_typed(const uint8_t* a, const uint8_t* sa, const uint8_t* b,
   if (M > 64 && scale_slices && slab_a < (1ll << 31) && slab_b < (1ll << 31) &&
       M * (K / 32) < (1ll << 31) && N * (K / 32) < (1ll << 31))
     return launch_tiled<AE, BE>(a, sa, b, sb, c, M, N, K, accumulate, stream);
-  const int64_t tiles = ((M + 15) / 16) * ((N + 15) / 16);
-  const int64_t grid = (tiles + 3) / 4;
-  hipLaunchKernelGGL((block_matmul_simple<AE, BE>), dim3((unsigned)grid), dim3(256), 0, stream,
-                     a, sa, b, sb, c, M, N, K, accumulate);
-  return hipGetLastError();
+  return launch_skinny<AE, BE>(a, sa, b, sb, c, M, N, K, accumulate, stream);
 }
 
 }  // namespace
