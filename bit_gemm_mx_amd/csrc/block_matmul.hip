@@ -236,32 +236,32 @@ block_matmul_skinny(const uint8_t* __restrict__ a, const uint8_t* __restrict__ s
 }
 
 // ---------------------------------------------------------------------------
-// Tiled kernel: 256x256 output tile per workgroup of 4 waves (2 x 2), each
-// wave 128x128 = 4 x 4 tiles of the 32x32x64 scaled MFMA.
+// Tiled kernel: 256x256 output tile per workgroup of 2 x WN waves, each wave
+// 128 x (256 / WN) = 4 x (8 / WN) tiles of the 32x32x64 scaled MFMA.
 //
-// K runs in stages of 128 elements (two MFMA K steps).  Code tiles are staged
-// straight into LDS by buffer loads that write LDS, kStages buffers deep; an
-// FP8 row of a stage is one whole 128-byte cache line.  Scale bytes are staged
-// the same way, 16 per row (512 K elements, a "scale chunk" of 4 stages) in
-// one load per row, double-buffered by chunk parity.  Every global load of the
-// main loop thus writes LDS and is covered by the explicit waits before the
-// barriers; operand and scale registers only wait on LDS reads.
+// K runs in stages of TK elements (TK / 64 MFMA K steps).  Code tiles are
+// staged straight into LDS by buffer loads that write LDS, two or four stage
+// buffers deep (as many as fit; an FP8 x FP8 stage of 128 K is 64 KiB).
+// Scale bytes are staged the same way, 16 per row (512 K elements, a "scale
+// chunk" of 512 / TK stages) in one load per row, double-buffered by chunk
+// parity.  Every global load of the main loop thus writes LDS and is covered
+// by the explicit waits before the barriers; operand and scale registers only
+// wait on LDS reads.
 // ---------------------------------------------------------------------------
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int kTM = 256, kTN = 256, kTK = 128, kTThreads = 256;
-constexpr int kChunkStages = 4;                   // stages per scale chunk
+constexpr int kTM = 256, kTN = 256;
 constexpr int kScaleRowBytes = 16;                // scale bytes per row per chunk
 constexpr int kScaleBytes = 2 * 256 * kScaleRowBytes;  // A and B rows of one chunk
 
-template <int ELEM>
+template <int ELEM, int TK, int WAVES = 4>
 struct Stage {
-  static constexpr int kRowBytes = ELEM == kE2M1 ? kTK / 2 : kTK;  // 64 or 128
+  static constexpr int kRowBytes = ELEM == kE2M1 ? TK / 2 : TK;     // 32 .. 128
   static constexpr int kChunks = kRowBytes / 16;                     // 16-B chunks per row
   static constexpr int kRowsPerLine = 256 / kRowBytes;               // rows per 256-B line
   static constexpr int kBytes = 256 * kRowBytes;                     // one 256-row tile
-  static constexpr int kInstr = kBytes / 1024 / 4;                   // 1-KiB loads per wave
+  static constexpr int kInstr = kBytes / 1024 / WAVES;               // 1-KiB loads per wave
 };
 
 // LDS byte offset of 16-byte chunk c of row r of a staged tile.  Rows are
@@ -270,9 +270,9 @@ struct Stage {
 // XOR-swizzled with the line index, so that the 16 lanes reading the same
 // logical chunk of 16 consecutive rows (an MFMA operand read) address 16
 // different 16-byte bank groups.
-template <int ELEM>
+template <int ELEM, int TK>
 __device__ __forceinline__ int lds_off(int r, int c) {
-  using S = Stage<ELEM>;
+  using S = Stage<ELEM, TK>;
   const int line = r / S::kRowsPerLine;
   const int q = (r % S::kRowsPerLine) * S::kChunks + c;
   return line * 256 + ((q ^ (line % S::kChunks)) << 4);
@@ -294,9 +294,9 @@ constexpr uint32_t kOutOfRange = 0x80000000u;  // past every resource used here
 // each lane fetches that chunk from global memory.  Lane i covers line
 // 4j + i/16 of instruction j; L % kChunks depends on the lane and, for 8 chunks
 // per row, on the parity of j, so two lane offsets are kept.
-template <int ELEM>
+template <int ELEM, int TK, int WAVES>
 struct Stager {
-  using S = Stage<ELEM>;
+  using S = Stage<ELEM, TK, WAVES>;
   uint32_t lane_off[2];  // row-in-instruction * row_bytes + 16 * chunk (even / odd j)
   uint32_t chunk16[2];   // 16 * chunk
   uint32_t instr_step;   // bytes between consecutive instructions' first rows
@@ -332,15 +332,15 @@ struct Stager {
   }
 };
 
-// MFMA operand of row r for K step h (0/1) of a staged tile.
-template <int ELEM>
+// MFMA operand of row r for K step h of a staged tile.
+template <int ELEM, int TK>
 __device__ __forceinline__ v8i read_operand(const uint8_t* lds, int r, int h, int g) {
   if (ELEM == kE4M3) {
-    const v4i lo = *reinterpret_cast<const v4i*>(lds + lds_off<ELEM>(r, 4 * h + g));
-    const v4i hi = *reinterpret_cast<const v4i*>(lds + lds_off<ELEM>(r, 4 * h + 2 + g));
+    const v4i lo = *reinterpret_cast<const v4i*>(lds + lds_off<ELEM, TK>(r, 4 * h + g));
+    const v4i hi = *reinterpret_cast<const v4i*>(lds + lds_off<ELEM, TK>(r, 4 * h + 2 + g));
     return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
   } else {
-    const v4i lo = *reinterpret_cast<const v4i*>(lds + lds_off<ELEM>(r, 2 * h + g));
+    const v4i lo = *reinterpret_cast<const v4i*>(lds + lds_off<ELEM, TK>(r, 2 * h + g));
     return v8i{lo.x, lo.y, lo.z, lo.w, 0, 0, 0, 0};
   }
 }
@@ -349,16 +349,24 @@ __device__ __forceinline__ v8i read_operand(const uint8_t* lds, int r, int h, in
 // memory operations are outstanding, leaving the other counters alone.
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
-template <int AE, int BE>
+template <int AE, int BE, int TK, int WN>
 struct Pipe {
-  // Stage buffers: as many as fit next to two scale chunks in 160 KiB.
-  static constexpr int kAB = Stage<AE>::kBytes + Stage<BE>::kBytes;
-  static constexpr int kStages = kAB <= 32768 ? 4 : 2;
+  static constexpr int kTK = TK;
+  static constexpr int kWaves = 2 * WN;                  // 2 along M, WN along N
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kWaveN = 256 / WN;                // columns of C per wave
+  static constexpr int kNQ = kWaveN / 32;                // 32x32 MFMA tiles along N per wave
+  static constexpr int kSteps = kTK / 64;                // MFMA K steps per stage
+  static constexpr int kChunkStages = 512 / kTK;         // stages per scale chunk
+  static constexpr int kAB = Stage<AE, kTK>::kBytes + Stage<BE, kTK>::kBytes;
+  // As many stage buffers (4 or 2) as fit next to two scale chunks in 160 KiB.
+  static constexpr int kStages = 4 * kAB + 2 * kScaleBytes <= 160 * 1024 ? 4 : 2;
   // Stages walked per loop iteration: whole scale chunks of both parities.
   static constexpr int kUnroll = 2 * kChunkStages;
   static_assert(kUnroll % kStages == 0, "buffer slots must repeat within the unrolled body");
-  static constexpr int kDma = Stage<AE>::kInstr + Stage<BE>::kInstr;  // per wave and stage
-  static constexpr int kScaleDma = 2;                                  // per wave and chunk
+  static constexpr int kDma = Stage<AE, kTK, kWaves>::kInstr + Stage<BE, kTK, kWaves>::kInstr;
+  // Scale chunk: 512 rows (A then B^T) of 16 bytes, 64 rows per load.
+  static constexpr int kScaleDma = 8 / kWaves;           // per wave and chunk
   // Loads a wave issues along with stage s: its code tiles, plus the scale
   // chunk that starts with it.
   static constexpr int ops(int s) { return kDma + (s % kChunkStages == 0 ? kScaleDma : 0); }
@@ -371,14 +379,16 @@ struct Pipe {
   }
 };
 
-template <int AE, int BE>
-__global__ void __launch_bounds__(kTThreads)
+template <int AE, int BE, int TK, int WN>
+__global__ void __launch_bounds__(128 * WN)
 block_matmul_tiled(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa,
                    const uint8_t* __restrict__ b, const uint8_t* __restrict__ sb,
                    float* __restrict__ c, int64_t M, int64_t N, int64_t K, int accumulate,
                    int tiles_m, int tiles_n) {
-  using P = Pipe<AE, BE>;
-  constexpr int kA = Stage<AE>::kBytes, kAB = P::kAB, kStages = P::kStages;
+  using P = Pipe<AE, BE, TK, WN>;
+  constexpr int kTK = P::kTK, kChunkStages = P::kChunkStages, kWaves = P::kWaves;
+  constexpr int kA = Stage<AE, kTK>::kBytes, kAB = P::kAB, kStages = P::kStages;
+  constexpr int kNQ = P::kNQ;
   // One array per buffer, always indexed by a compile-time slot, so that the
   // compiler can tell the direct-to-LDS loads into one buffer from the reads
   // of another and keep the loads in flight.
@@ -406,12 +416,12 @@ block_matmul_tiled(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa
 
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int wm = wave >> 1, wn = wave & 1, g = lane >> 5, lr = lane & 31;
+  const int wm = wave / WN, wn = wave % WN, g = lane >> 5, lr = lane & 31;
   const uint32_t Ku = (uint32_t)K;
   const uint32_t a_row_bytes = AE == kE2M1 ? Ku / 2 : Ku;
   const uint32_t b_row_bytes = BE == kE2M1 ? Ku / 2 : Ku;
-  const Stager<AE> stage_a(a_row_bytes, lane);
-  const Stager<BE> stage_b(b_row_bytes, lane);
+  const Stager<AE, kTK, kWaves> stage_a(a_row_bytes, lane);
+  const Stager<BE, kTK, kWaves> stage_b(b_row_bytes, lane);
   const uint32_t kblocks = Ku / 32;
   const int64_t rows_a = min(M - m0, (int64_t)kTM), rows_b = min(N - n0, (int64_t)kTN);
   // (a 256-row slab of either operand is below 2^31 bytes: checked at launch)
@@ -419,16 +429,14 @@ block_matmul_tiled(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(b + n0 * b_row_bytes, rows_b * b_row_bytes);
   const __amdgpu_buffer_rsrc_t rsa = make_rsrc(sa + m0 * kblocks, rows_a * kblocks);
   const __amdgpu_buffer_rsrc_t rsb = make_rsrc(sb + n0 * kblocks, rows_b * kblocks);
-  const int ar = wm * 128 + lr, br = wn * 128 + lr;  // this lane's first A / B^T tile row
-  // Scale staging: wave w fetches rows [64w, 64w+64) of A and of B^T, one
-  // 16-byte row slice per lane (blocks [16 * chunk, 16 * chunk + 16)).
-  const uint32_t scale_lane_off = (uint32_t)(64 * wave + lane) * kblocks;
+  // This lane's first A / B^T tile row.
+  const int ar = wm * 128 + lr, br = wn * P::kWaveN + lr;
 
-  v16f acc[4][4];
+  v16f acc[4][kNQ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kNQ; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
@@ -436,20 +444,25 @@ block_matmul_tiled(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa
     return buf == 0 ? smem0 : buf == 1 ? smem1 : buf == 2 ? smem2 : smem3;
   };
   // Issue stage st into buffer (st % kStages); the first stage of a scale
-  // chunk also fetches the chunk's scales into the set of the chunk's parity.
+  // chunk also fetches the chunk's scales into the set of the chunk's parity:
+  // the 512 rows of the chunk (A's 256, then B^T's) as 16-byte row slices
+  // (blocks [16 * chunk, 16 * chunk + 16)), 64 rows per load, rows in order.
   auto issue = [&](int st, int buf, int par) {
     uint8_t* dst = slot(buf);
-    stage_a.load(dst, ra, a_row_bytes, (uint32_t)st * Stage<AE>::kRowBytes, wave);
-    stage_b.load(dst + kA, rb, b_row_bytes, (uint32_t)st * Stage<BE>::kRowBytes, wave);
+    stage_a.load(dst, ra, a_row_bytes, (uint32_t)st * Stage<AE, kTK>::kRowBytes, wave);
+    stage_b.load(dst + kA, rb, b_row_bytes, (uint32_t)st * Stage<BE, kTK>::kRowBytes, wave);
     if (st % kChunkStages == 0) {
       const uint32_t kb = (uint32_t)(st / kChunkStages) * kScaleRowBytes;
-      const uint32_t off = kb < kblocks ? scale_lane_off : kOutOfRange;
-      uint8_t* sdst = (par ? scales1 : scales0) + wave * 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsa, (__attribute__((address_space(3))) void*)sdst, 16, off, kb, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsb, (__attribute__((address_space(3))) void*)(sdst + kScaleBytes / 2), 16, off, kb, 0,
-          0);
+#pragma unroll
+      for (int j = 0; j < P::kScaleDma; ++j) {
+        const int part = wave * P::kScaleDma + j;  // 64-row part of the 512 rows
+        const uint32_t off = kb < kblocks ? (uint32_t)(64 * (part & 3) + lane) * kblocks
+                                          : kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            part < 4 ? rsa : rsb,
+            (__attribute__((address_space(3))) void*)((par ? scales1 : scales0) + part * 1024),
+            16, off, kb, 0, 0);
+      }
     }
   };
 
@@ -478,40 +491,43 @@ block_matmul_tiled(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa
     const uint8_t* la = slot(buf);
     const uint8_t* lb = la + kA;
     const uint8_t* sc = par ? scales1 : scales0;
-    // Scale dword of this stage (blocks [4 sub, 4 sub + 4) of the chunk) of
-    // each row, shifted so that byte 0 / byte 2 hold this lane's block of
-    // K step 0 / 1 (lane group g takes block g of each step).
-    int sas[4], sbs[4];
+    // The stage covers blocks [blk0, blk0 + kTK/32) of the chunk.  Read the
+    // scale dword holding them, shifted so that byte sel0 + 2h holds this
+    // lane's block of K step h (lane group g takes block g of each step).
+    constexpr int blk0 = sub * (kTK / 32), sel0 = blk0 % 4;
+    int sas[4], sbs[kNQ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i)
       sas[i] = (int)(*reinterpret_cast<const uint32_t*>(sc + (ar + 32 * i) * kScaleRowBytes +
-                                                        4 * sub) >> (8 * g));
-      sbs[i] = (int)(*reinterpret_cast<const uint32_t*>(sc + kScaleBytes / 2 +
-                                                        (br + 32 * i) * kScaleRowBytes +
-                                                        4 * sub) >> (8 * g));
-    }
+                                                        (blk0 & ~3)) >> (8 * g));
+#pragma unroll
+    for (int q = 0; q < kNQ; ++q)
+      sbs[q] = (int)(*reinterpret_cast<const uint32_t*>(sc + kScaleBytes / 2 +
+                                                        (br + 32 * q) * kScaleRowBytes +
+                                                        (blk0 & ~3)) >> (8 * g));
     auto kstep = [&](auto H) {
       constexpr int h = decltype(H)::value;
-      v8i af[4], bf[4];
+      v8i af[4], bf[kNQ];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = read_operand<AE>(la, ar + 32 * i, h, g);
+      for (int i = 0; i < 4; ++i) af[i] = read_operand<AE, kTK>(la, ar + 32 * i, h, g);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) bf[q] = read_operand<BE>(lb, br + 32 * q, h, g);
+      for (int q = 0; q < kNQ; ++q) bf[q] = read_operand<BE, kTK>(lb, br + 32 * q, h, g);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < kNQ; ++q)
           acc[i][q] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              af[i], bf[q], acc[i][q], Operand<AE>::kFmt, Operand<BE>::kFmt, 2 * h, sas[i],
-              2 * h, sbs[q]);
+              af[i], bf[q], acc[i][q], Operand<AE>::kFmt, Operand<BE>::kFmt, sel0 + 2 * h,
+              sas[i], sel0 + 2 * h, sbs[q]);
     };
     kstep(std::integral_constant<int, 0>{});
-    kstep(std::integral_constant<int, 1>{});
+    if constexpr (P::kSteps > 1) kstep(std::integral_constant<int, 1>{});
     // Instruction order for the scheduler: the operand and scale reads of the
     // first K step, then one MFMA, one global load and one LDS read at a
     // time, so that the loads of the next stage drain through the memory
     // pipeline while the MFMAs run instead of stalling the wave in a burst.
-    constexpr int kMfma = 32, kVmem = P::kDma + (nu % kChunkStages == 0 ? P::kScaleDma : 0);
+    constexpr int kMfma = 4 * kNQ * P::kSteps;
+    constexpr int kVmem = P::kDma + (nu % kChunkStages == 0 ? P::kScaleDma : 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);  // LDS reads
 #pragma unroll
     for (int k = 0; k < kMfma; ++k) {
@@ -529,6 +545,16 @@ block_matmul_tiled(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa
     stage(std::integral_constant<int, 5>{});
     stage(std::integral_constant<int, 6>{});
     stage(std::integral_constant<int, 7>{});
+    if constexpr (P::kUnroll > 8) {
+      stage(std::integral_constant<int, 8>{});
+      stage(std::integral_constant<int, 9>{});
+      stage(std::integral_constant<int, 10>{});
+      stage(std::integral_constant<int, 11>{});
+      stage(std::integral_constant<int, 12>{});
+      stage(std::integral_constant<int, 13>{});
+      stage(std::integral_constant<int, 14>{});
+      stage(std::integral_constant<int, 15>{});
+    }
   }
   // No load may still be writing this workgroup's LDS when it exits.
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -537,8 +563,8 @@ block_matmul_tiled(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t col = n0 + wn * 128 + 32 * q + lr;
+    for (int q = 0; q < kNQ; ++q) {
+      const int64_t col = n0 + wn * P::kWaveN + 32 * q + lr;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int64_t row = m0 + wm * 128 + 32 * i + 8 * (e >> 2) + 4 * g + (e & 3);
@@ -551,14 +577,20 @@ block_matmul_tiled(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa
     }
 }
 
+// Launch configuration: 128-element K stages, 8 waves (2 x 4, 128 x 64 of C
+// each).  Two waves per SIMD let one wave's MFMAs run while the other waits
+// on LDS reads, its loads or the barrier.
+constexpr int kTiledTK = 128, kTiledWN = 4;
+
 template <int AE, int BE>
 hipError_t launch_tiled(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
                         float* c, int64_t M, int64_t N, int64_t K, int accumulate,
                         hipStream_t stream) {
+  constexpr int TK = kTiledTK, WN = kTiledWN;
   const int64_t tiles_m = (M + kTM - 1) / kTM, tiles_n = (N + kTN - 1) / kTN;
-  hipLaunchKernelGGL((block_matmul_tiled<AE, BE>), dim3((unsigned)(tiles_m * tiles_n)),
-                     dim3(kTThreads), 0, stream, a, sa, b, sb, c, M, N, K, accumulate,
-                     (int)tiles_m, (int)tiles_n);
+  hipLaunchKernelGGL((block_matmul_tiled<AE, BE, TK, WN>), dim3((unsigned)(tiles_m * tiles_n)),
+                     dim3(Pipe<AE, BE, TK, WN>::kThreads), 0, stream, a, sa, b, sb, c, M, N, K,
+                     accumulate, (int)tiles_m, (int)tiles_n);
   return hipGetLastError();
 }
 
