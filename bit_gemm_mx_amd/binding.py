@@ -48,6 +48,12 @@ def lib() -> ctypes.CDLL:
     L.mx_dequantize.restype = i32
     L.mx_block_matmul.argtypes = [p, p, i32, p, p, i32, p, i64, i64, i64, i32, i32, p]
     L.mx_block_matmul.restype = i32
+    L.mx_quantize_axis.argtypes = [p, p, p, i64, i64, i32, i32, i32, p]
+    L.mx_quantize_axis.restype = i32
+    L.mx_dequantize_axis.argtypes = [p, p, p, i64, i64, i32, i32, i32, p]
+    L.mx_dequantize_axis.restype = i32
+    L.mx_fold_scale.argtypes = [p, i64, i32, p]
+    L.mx_fold_scale.restype = i32
     L.mx_codes_bytes.argtypes = [i64, i64, i32]
     L.mx_codes_bytes.restype = sz
     L.mx_num_scale_blocks.argtypes = [i64, i64, i32]
@@ -72,6 +78,22 @@ def mx_quantize(x_ptr, codes_ptr, scales_ptr, rows, cols, elem, block_size=BLOCK
 
 def mx_dequantize(codes_ptr, scales_ptr, y_ptr, rows, cols, elem, block_size=BLOCK, stream=None):
     _check(lib().mx_dequantize(codes_ptr, scales_ptr, y_ptr, rows, cols, elem, block_size, stream))
+
+
+def mx_quantize_axis(x_ptr, codes_ptr, scales_ptr, rows, cols, axis, elem, block_size=BLOCK,
+                     stream=None):
+    _check(lib().mx_quantize_axis(x_ptr, codes_ptr, scales_ptr, rows, cols, axis, elem,
+                                  block_size, stream))
+
+
+def mx_dequantize_axis(codes_ptr, scales_ptr, y_ptr, rows, cols, axis, elem, block_size=BLOCK,
+                       stream=None):
+    _check(lib().mx_dequantize_axis(codes_ptr, scales_ptr, y_ptr, rows, cols, axis, elem,
+                                    block_size, stream))
+
+
+def mx_fold_scale(scales_ptr, n_scales, j, stream=None):
+    _check(lib().mx_fold_scale(scales_ptr, n_scales, j, stream))
 
 
 def mx_block_matmul(a_codes, a_scales, a_elem, b_codes, b_scales, b_elem, c, M, N, K,
@@ -118,64 +140,87 @@ def _require(t, dtype, name):
 class MXTensor:
     """A block-scaled [rows, cols] tensor: element codes plus E8M0 scales.
 
-    codes: uint8 [rows, cols/2] (E2M1, element 2j in the low nibble of byte j)
-           or uint8 [rows, cols] (E4M3);  scales: uint8 [rows, cols/32].
+    axis = 1 (blocks along the last axis):
+      codes: uint8 [rows, cols/2] (E2M1, element 2j in the low nibble of byte j)
+             or uint8 [rows, cols] (E4M3);  scales: uint8 [rows, cols/32].
+    axis = 0 (blocks along axis 0), block-major storage, the layout of the
+      transposed matrix: codes [cols, rows/2 or rows], scales [cols, rows/32].
     """
     codes: "object"
     scales: "object"
     rows: int
     cols: int
     elem: int
+    axis: int = 1
 
     @property
     def device(self):
         return self.codes.device
 
 
-def empty_mx(rows: int, cols: int, elem: int, device) -> MXTensor:
+def empty_mx(rows: int, cols: int, elem: int, device, axis: int = 1) -> MXTensor:
     import torch
-    nbytes = mx_codes_bytes(rows, cols, elem)
-    width = nbytes // rows if rows else 0
-    codes = torch.empty((rows, width), dtype=torch.uint8, device=device)
-    scales = torch.empty((rows, cols // BLOCK), dtype=torch.uint8, device=device)
-    return MXTensor(codes, scales, rows, cols, elem)
+    # storage is that of the [rows, cols] matrix blocked along its last axis,
+    # or of its transpose when blocked along axis 0
+    sr, sc = (rows, cols) if axis == 1 else (cols, rows)
+    nbytes = mx_codes_bytes(sr, sc, elem)
+    width = nbytes // sr if sr else 0
+    codes = torch.empty((sr, width), dtype=torch.uint8, device=device)
+    scales = torch.empty((sr, sc // BLOCK), dtype=torch.uint8, device=device)
+    return MXTensor(codes, scales, rows, cols, elem, axis)
 
 
-def quantize(x, elem: int = MX_E2M1, out: MXTensor | None = None) -> MXTensor:
-    """float32 [rows, cols] GPU tensor -> MXTensor (mx_quantize)."""
+def quantize(x, elem: int = MX_E2M1, out: MXTensor | None = None, axis: int = 1) -> MXTensor:
+    """float32 [rows, cols] GPU tensor -> MXTensor blocked along `axis`
+    (mx_quantize, or mx_quantize_axis for axis 0)."""
     import torch
     _require(x, torch.float32, "x")
     if x.dim() != 2:
         raise ValueError("x must be 2-D [rows, cols]")
     rows, cols = x.shape
     if out is None:
-        out = empty_mx(rows, cols, elem, x.device)
+        out = empty_mx(rows, cols, elem, x.device, axis)
+    if (out.rows, out.cols, out.elem, out.axis) != (rows, cols, elem, axis):
+        raise ValueError("out does not describe x's shape, element type and block axis")
     _require(out.codes, torch.uint8, "codes")
     _require(out.scales, torch.uint8, "scales")
-    mx_quantize(x.data_ptr(), out.codes.data_ptr(), out.scales.data_ptr(), rows, cols, elem,
-                BLOCK, _stream_ptr(x.device))
+    mx_quantize_axis(x.data_ptr(), out.codes.data_ptr(), out.scales.data_ptr(), rows, cols,
+                     axis, elem, BLOCK, _stream_ptr(x.device))
     return out
 
 
 def dequantize(t: MXTensor, out=None):
-    """MXTensor -> float32 [rows, cols] GPU tensor (mx_dequantize)."""
+    """MXTensor -> float32 [rows, cols] GPU tensor (mx_dequantize_axis)."""
     import torch
     _require(t.codes, torch.uint8, "codes")
     _require(t.scales, torch.uint8, "scales")
     if out is None:
         out = torch.empty((t.rows, t.cols), dtype=torch.float32, device=t.codes.device)
     _require(out, torch.float32, "out")
-    mx_dequantize(t.codes.data_ptr(), t.scales.data_ptr(), out.data_ptr(), t.rows, t.cols,
-                  t.elem, BLOCK, _stream_ptr(out.device))
+    mx_dequantize_axis(t.codes.data_ptr(), t.scales.data_ptr(), out.data_ptr(), t.rows, t.cols,
+                       t.axis, t.elem, BLOCK, _stream_ptr(out.device))
     return out
 
 
-def block_matmul(a: MXTensor, bt: MXTensor, out=None, accumulate: bool = False):
-    """C = [C +] A . B with A [M, K] and B given as B^T [N, K] (mx_block_matmul)."""
+def fold_scale(t: MXTensor, j: int) -> MXTensor:
+    """In place: t becomes 2^j * t through its scale bytes (mx_fold_scale)."""
     import torch
-    if a.cols != bt.cols:
-        raise ValueError(f"K mismatch: A has {a.cols}, B^T has {bt.cols}")
-    M, N, K = a.rows, bt.rows, a.cols
+    _require(t.scales, torch.uint8, "scales")
+    mx_fold_scale(t.scales.data_ptr(), t.scales.numel(), j, _stream_ptr(t.scales.device))
+    return t
+
+
+def block_matmul(a: MXTensor, bt: MXTensor, out=None, accumulate: bool = False):
+    """C = [C +] A . B with A [M, K] blocked along K, and B given either as
+    B^T [N, K] blocked along its last axis or as B [K, N] blocked along axis 0
+    (the same storage) (mx_block_matmul)."""
+    import torch
+    if a.axis != 1:
+        raise ValueError("A must be blocked along its last axis (K)")
+    bn, bk = (bt.rows, bt.cols) if bt.axis == 1 else (bt.cols, bt.rows)
+    if a.cols != bk:
+        raise ValueError(f"K mismatch: A has {a.cols}, B has {bk}")
+    M, N, K = a.rows, bn, a.cols
     if out is None:
         if accumulate:
             raise ValueError("accumulate=True needs an existing out tensor")

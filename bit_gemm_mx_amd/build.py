@@ -20,7 +20,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmx.so")
-SOURCES = ["libmx.cpp", "quantize.hip", "dequantize.hip", "block_matmul.hip"]
+SOURCES = ["libmx.cpp", "quantize.hip", "dequantize.hip", "codec_axis0.hip",
+           "scale_ops.hip", "block_matmul.hip"]
 ARCH = "gfx950"
 
 

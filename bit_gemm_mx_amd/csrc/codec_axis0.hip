@@ -1,0 +1,237 @@
+// MX quantize / dequantize with blocks along axis 0 of a row-major
+// [rows, cols] float32 matrix: block (i, c) = x[32i .. 32i+31, c].  The
+// dialect page "A Dialect Is a Set of Co-Designed Decisions", section "The
+// block axis": a block's scale must be constant along the reduction it
+// multiplies, so a K x N matrix B is blocked along axis 0.
+//
+// Storage is block-major: codes [cols, rows/2] (E2M1, element 2k of a
+// column's run in the low nibble of byte k) or [cols, rows] (E4M3), scales
+// [cols, rows/32] -- the layout mx_quantize gives for the transposed matrix,
+// which is the B^T operand layout of mx_block_matmul.  Element encode and
+// decode are those of the last-axis kernels (codec_common.h).
+//
+// Work mapping: lane l of a wave owns column c0 + l and the wave walks kRun
+// consecutive block-rows.  A row segment of 64 columns is 256 contiguous
+// bytes, so every load (quantize) and store (dequantize) instruction on the
+// float32 side is coalesced, and each lane holds its whole block in 32
+// registers: amax, exponent and rounding need no cross-lane traffic.  Per
+// lane, the codes of the kRun blocks are contiguous in memory (16 or 32 bytes
+// each) and so are their kRun scale bytes.
+#include "codec_common.h"
+
+namespace mx {
+namespace {
+
+using namespace codec;
+
+constexpr int kThreads = 256;
+constexpr int kRun = 8;  // block-rows per wave
+
+typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+
+// Wave task t -> (column strip, run of block-rows); consecutive tasks walk
+// down one strip, so the waves of a workgroup write adjacent bytes of the
+// same code and scale rows.
+struct Task {
+  int64_t c;   // this lane's column
+  int64_t i0;  // first block-row of the run
+  bool live;   // column inside the matrix
+};
+
+__device__ __forceinline__ Task task_of(int64_t cols, int64_t n_runs) {
+  const int64_t t = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  const int64_t strip = t / n_runs, run = t % n_runs;
+  Task k;
+  k.c = strip * 64 + lane;
+  k.i0 = run * kRun;
+  k.live = k.c < cols;
+  return k;
+}
+
+template <int ELEM>
+__device__ __forceinline__ void load_block(float (&v)[32], const float* __restrict__ x,
+                                           int64_t i, int64_t cols, const Task& k) {
+#pragma unroll
+  for (int j = 0; j < 32; ++j)
+    v[j] = k.live ? __builtin_nontemporal_load(&x[(32 * i + j) * cols + k.c]) : 0.f;
+}
+
+template <int ELEM>
+__global__ void __launch_bounds__(kThreads)
+quantize_axis0_kernel(const float* __restrict__ x, uint8_t* __restrict__ codes,
+                      uint8_t* __restrict__ scales, int64_t rows, int64_t cols, int64_t n_runs,
+                      int scale_vec) {
+  using F = Fmt<ELEM>;
+  const Task k = task_of(cols, n_runs);
+  const int64_t nbr = rows / 32;
+  if (k.i0 >= nbr) return;  // wave-uniform: past the last run of the strip
+  const int run = (int)min((int64_t)kRun, nbr - k.i0);
+  const int64_t row_bytes = ELEM == kE2M1 ? rows / 2 : rows;
+  constexpr int kBlockBytes = ELEM == kE2M1 ? 16 : 32;
+  uint8_t* crow = codes + k.c * row_bytes;
+  uint8_t* srow = scales + k.c * nbr;
+
+  uint32_t sbytes[kRun / 4] = {};
+  float v[32], nv[32];
+  load_block<ELEM>(v, x, k.i0, cols, k);
+  for (int r = 0; r < run; ++r) {
+    if (r + 1 < run) load_block<ELEM>(nv, x, k.i0 + r + 1, cols, k);
+    uint32_t amax = 0, low = 0xFFFFFFFFu;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const uint32_t b = __float_as_uint(v[j]);
+      amax = max(amax, b & 0x7FFFFFFFu);
+      low = min(low, b << F::kTieShift);
+    }
+    const int e = block_exponent<ELEM>(amax);
+    const bool nonfinite = amax >= 0x7F800000u;
+    const uint32_t byte = amax == 0 ? 127u : (nonfinite ? 0xFFu : (uint32_t)(e + 127));
+    const float inv_scale = __uint_as_float((uint32_t)(127 - e) << 23);
+    const float scale = __uint_as_float((uint32_t)max(e + 127, 1) << 23);
+    const bool exact = k.live && (low == 0 || amax < 0x0D800000u);
+    uint32_t w[8];  // codes of 4 consecutive elements each
+    if (__ballot(exact) == 0) {
+      const float top = ELEM == kE4M3 ? 448.0f * scale : 0.0f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        w[q] = convert4<ELEM>(make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]),
+                              scale, top);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        w[q] = round4<ELEM>(make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]),
+                            inv_scale);
+    }
+    if (nonfinite) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) w[q] = 0;
+    }
+    if (k.live) {
+      const int64_t i = k.i0 + r;
+      if (ELEM == kE2M1) {
+        const u4v d = {w[0] | (w[1] << 16), w[2] | (w[3] << 16), w[4] | (w[5] << 16),
+                       w[6] | (w[7] << 16)};
+        *reinterpret_cast<u4v*>(crow + i * kBlockBytes) = d;
+      } else {
+        const u4v d0 = {w[0], w[1], w[2], w[3]}, d1 = {w[4], w[5], w[6], w[7]};
+        *reinterpret_cast<u4v*>(crow + i * kBlockBytes) = d0;
+        *reinterpret_cast<u4v*>(crow + i * kBlockBytes + 16) = d1;
+      }
+      if (scale_vec)
+        sbytes[r >> 2] |= byte << (8 * (r & 3));
+      else
+        srow[i] = (uint8_t)byte;
+    }
+    if (r + 1 < run) {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) v[j] = nv[j];
+    }
+  }
+  // Whole runs with 8-byte aligned scale rows: one store of the run's bytes.
+  if (scale_vec && k.live)
+    *reinterpret_cast<uint2*>(srow + k.i0) = make_uint2(sbytes[0], sbytes[1]);
+}
+
+template <int ELEM>
+__global__ void __launch_bounds__(kThreads)
+dequantize_axis0_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                        float* __restrict__ y, int64_t rows, int64_t cols, int64_t n_runs,
+                        int scale_vec) {
+  const Task k = task_of(cols, n_runs);
+  const int64_t nbr = rows / 32;
+  if (k.i0 >= nbr) return;
+  const int run = (int)min((int64_t)kRun, nbr - k.i0);
+  const int64_t row_bytes = ELEM == kE2M1 ? rows / 2 : rows;
+  constexpr int kBlockBytes = ELEM == kE2M1 ? 16 : 32;
+  const uint8_t* crow = codes + k.c * row_bytes;
+  const uint8_t* srow = scales + k.c * nbr;
+
+  uint2 sv = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
+  if (scale_vec && k.live) sv = *reinterpret_cast<const uint2*>(srow + k.i0);
+  for (int r = 0; r < run; ++r) {
+    const int64_t i = k.i0 + r;
+    u4v d0 = {0, 0, 0, 0}, d1 = {0, 0, 0, 0};
+    uint32_t byte = 127;
+    if (k.live) {
+      d0 = *reinterpret_cast<const u4v*>(crow + i * kBlockBytes);
+      if (ELEM == kE4M3) d1 = *reinterpret_cast<const u4v*>(crow + i * kBlockBytes + 16);
+      byte = scale_vec ? (((r < 4 ? sv.x : sv.y) >> (8 * (r & 3))) & 0xFFu) : srow[i];
+    }
+    const float s = scale_value(byte);
+    uint32_t o[32];
+    if (ELEM == kE2M1) {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) o[j] = decode_e2m1(d0[j >> 3] >> (4 * (j & 7)), s);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const uint32_t word = j < 16 ? d0[j >> 2] : d1[(j - 16) >> 2];
+        o[j] = decode_e4m3((word >> (8 * (j & 3))) & 0xFFu, s);
+      }
+    }
+    if (byte == 0xFFu) {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) o[j] = kNaN;
+    }
+    if (k.live) {
+#pragma unroll
+      for (int j = 0; j < 32; ++j)
+        __builtin_nontemporal_store(__uint_as_float(o[j]), &y[(32 * i + j) * cols + k.c]);
+    }
+  }
+}
+
+struct Launch {
+  dim3 grid;
+  int64_t n_runs;
+  int scale_vec;
+};
+
+Launch plan(const uint8_t* scales, int64_t rows, int64_t cols) {
+  const int64_t nbr = rows / 32;
+  const int64_t n_runs = (nbr + kRun - 1) / kRun;
+  const int64_t strips = (cols + 63) / 64;
+  const int64_t waves = strips * n_runs;
+  Launch l;
+  l.grid = dim3((unsigned)((waves + kThreads / 64 - 1) / (kThreads / 64)));
+  l.n_runs = n_runs;
+  // Scale runs are stored / loaded as 8 bytes when every run is whole and
+  // every column's scale row starts on an 8-byte boundary.
+  l.scale_vec = (nbr % kRun == 0) && ((reinterpret_cast<uintptr_t>(scales) & 7) == 0);
+  return l;
+}
+
+}  // namespace
+
+hipError_t launch_quantize_axis0(const float* x, void* codes, uint8_t* scales, int64_t rows,
+                                 int64_t cols, int elem, hipStream_t stream) {
+  const Launch l = plan(scales, rows, cols);
+  if (l.grid.x == 0 || (int64_t)l.grid.x * (kThreads / 64) < ((cols + 63) / 64) * l.n_runs)
+    return hipErrorInvalidValue;
+  uint8_t* c = static_cast<uint8_t*>(codes);
+  if (elem == kE2M1)
+    hipLaunchKernelGGL(quantize_axis0_kernel<kE2M1>, l.grid, dim3(kThreads), 0, stream, x, c,
+                       scales, rows, cols, l.n_runs, l.scale_vec);
+  else
+    hipLaunchKernelGGL(quantize_axis0_kernel<kE4M3>, l.grid, dim3(kThreads), 0, stream, x, c,
+                       scales, rows, cols, l.n_runs, l.scale_vec);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize_axis0(const void* codes, const uint8_t* scales, float* y,
+                                   int64_t rows, int64_t cols, int elem, hipStream_t stream) {
+  const Launch l = plan(scales, rows, cols);
+  if (l.grid.x == 0 || (int64_t)l.grid.x * (kThreads / 64) < ((cols + 63) / 64) * l.n_runs)
+    return hipErrorInvalidValue;
+  const uint8_t* c = static_cast<const uint8_t*>(codes);
+  if (elem == kE2M1)
+    hipLaunchKernelGGL(dequantize_axis0_kernel<kE2M1>, l.grid, dim3(kThreads), 0, stream, c,
+                       scales, y, rows, cols, l.n_runs, l.scale_vec);
+  else
+    hipLaunchKernelGGL(dequantize_axis0_kernel<kE4M3>, l.grid, dim3(kThreads), 0, stream, c,
+                       scales, y, rows, cols, l.n_runs, l.scale_vec);
+  return hipGetLastError();
+}
+
+}  // namespace mx

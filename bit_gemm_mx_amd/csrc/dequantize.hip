@@ -1,48 +1,20 @@
-// MX dequantize: E2M1 / E4M3 codes + E8M0 scales -> float32.
-//
-// Semantics follow the "Bit Layout" page (mxfp4community.com), sections
-// "The E8M0 shared scale" (value 2^(byte-127), byte 0xFF poisons the block to
-// NaN) and "Reference encode and decode" (sign x table[magnitude] x scale,
-// exact).  E4M3 codes 0x7F / 0xFF are f8E4M3FN NaN.
-//
-// Decoding without tables: placing the element's exponent and mantissa bits
-// at the top of a float32 mantissa field and multiplying by a power of two
-// reproduces the element value exactly (E2M1: magnitude bits << 22, times
-// 2^126; E4M3: magnitude bits << 20, times 2^120), subnormal element codes
-// included, because f32 arithmetic keeps denormals (IEEE mode, no flushing).
-// The second multiply by the block scale is exact as well.
+// MX dequantize: E2M1 / E4M3 codes + E8M0 scales -> float32, blocks along the
+// last axis.  Table-free exact decode is in codec_common.h.
 //
 // Work mapping mirrors the quantize kernel: 8 lanes per block, each lane
 // writes one 16-byte float4, so a wave's store instruction writes 1 KiB of
 // contiguous memory; kUnroll independent blocks per lane and iteration.
-#include "mx_internal.h"
+#include "codec_common.h"
 
 namespace mx {
 namespace {
 
+using namespace codec;
+
 constexpr int kThreads = 256;
 constexpr int kUnroll = 4;
 constexpr int kBlocksPerWaveIter = 8 * kUnroll;
-constexpr uint32_t kNaN = 0x7FC00000u;
 typedef float f4v __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ float scale_value(uint32_t byte) {
-  // 2^(byte-127); byte 0 is the float32 subnormal 2^-127.
-  return __uint_as_float(byte ? (byte << 23) : 0x00400000u);
-}
-
-// Nibble n (sign in bit 3) of an E2M1 code -> float bits, scaled.
-__device__ __forceinline__ uint32_t decode_e2m1(uint32_t n, float scale) {
-  const float mag = __uint_as_float((n & 7u) << 22) * 0x1p126f;
-  return __float_as_uint(mag * scale) | ((n & 8u) << 28);
-}
-
-// Byte c of an E4M3 code -> float bits, scaled (NaN codes handled by caller).
-__device__ __forceinline__ uint32_t decode_e4m3(uint32_t c, float scale) {
-  const float mag = __uint_as_float((c & 0x7Fu) << 20) * 0x1p120f;
-  const uint32_t v = __float_as_uint(mag * scale) | ((c & 0x80u) << 24);
-  return (c & 0x7Fu) == 0x7Fu ? kNaN : v;
-}
 
 template <int ELEM>
 __global__ void __launch_bounds__(kThreads)

@@ -65,6 +65,36 @@ mx_status_t mx_block_matmul(const void* a_codes, const uint8_t* a_scales, mx_ele
                                           reinterpret_cast<hipStream_t>(stream)));
 }
 
+mx_status_t mx_quantize_axis(const float* x, void* codes, uint8_t* scales, int64_t rows,
+                             int64_t cols, int32_t axis, mx_elem_t elem, int32_t block_size,
+                             mx_stream_t stream) {
+  if (axis == 1) return mx_quantize(x, codes, scales, rows, cols, elem, block_size, stream);
+  if (axis != 0) return MX_ERR_UNSUPPORTED;
+  // Blocks along axis 0 are the blocks of the transposed [cols, rows] matrix.
+  const mx_status_t s = check_codec(x, codes, scales, cols, rows, elem, block_size);
+  if (s != MX_OK) return s;
+  return from_hip(mx::launch_quantize_axis0(x, codes, scales, rows, cols, (int)elem,
+                                            reinterpret_cast<hipStream_t>(stream)));
+}
+
+mx_status_t mx_dequantize_axis(const void* codes, const uint8_t* scales, float* y, int64_t rows,
+                               int64_t cols, int32_t axis, mx_elem_t elem, int32_t block_size,
+                               mx_stream_t stream) {
+  if (axis == 1) return mx_dequantize(codes, scales, y, rows, cols, elem, block_size, stream);
+  if (axis != 0) return MX_ERR_UNSUPPORTED;
+  const mx_status_t s = check_codec(y, codes, scales, cols, rows, elem, block_size);
+  if (s != MX_OK) return s;
+  return from_hip(mx::launch_dequantize_axis0(codes, scales, y, rows, cols, (int)elem,
+                                              reinterpret_cast<hipStream_t>(stream)));
+}
+
+mx_status_t mx_fold_scale(uint8_t* scales, int64_t n_scales, int32_t j, mx_stream_t stream) {
+  if (!scales) return MX_ERR_NULL;
+  if (n_scales < 1) return MX_ERR_SHAPE;
+  return from_hip(mx::launch_fold_scale(scales, n_scales, (int)j,
+                                        reinterpret_cast<hipStream_t>(stream)));
+}
+
 size_t mx_codes_bytes(int64_t rows, int64_t cols, mx_elem_t elem) {
   if (rows < 0 || cols < 0 || !is_elem(elem)) return 0;
   if (cols != 0 && rows > INT64_MAX / cols) return 0;

@@ -17,6 +17,16 @@ hipError_t launch_quantize(const float* x, void* codes, uint8_t* scales, int64_t
 hipError_t launch_dequantize(const void* codes, const uint8_t* scales, float* y,
                              int64_t n_blocks, int elem, hipStream_t stream);
 
+// Codec with blocks along axis 0, block-major storage (codec_axis0.hip);
+// rows % 32 == 0.
+hipError_t launch_quantize_axis0(const float* x, void* codes, uint8_t* scales, int64_t rows,
+                                 int64_t cols, int elem, hipStream_t stream);
+hipError_t launch_dequantize_axis0(const void* codes, const uint8_t* scales, float* y,
+                                   int64_t rows, int64_t cols, int elem, hipStream_t stream);
+
+// scales[i] -> scales of 2^j times the tensor, in place (scale_ops.hip).
+hipError_t launch_fold_scale(uint8_t* scales, int64_t n, int j, hipStream_t stream);
+
 // Block-scaled matmul (block_matmul.hip).  C[M,N] (+)= A[M,K] . (B^T[N,K])^T.
 hipError_t launch_block_matmul(const void* a_codes, const uint8_t* a_scales, int a_elem,
                                const void* b_codes, const uint8_t* b_scales, int b_elem,

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define LIBMX_ABI_VERSION 1
+#define LIBMX_ABI_VERSION 2
 #define MX_BLOCK_SIZE 32
 
 /* Same object as HIP's hipStream_t (a pointer to the runtime's stream). */
@@ -118,6 +118,46 @@ mx_status_t mx_block_matmul(const void *a_codes, const uint8_t *a_scales, mx_ele
                             const void *b_codes, const uint8_t *b_scales, mx_elem_t b_elem,
                             float *c, int64_t M, int64_t N, int64_t K, int32_t block_size,
                             int32_t accumulate, mx_stream_t stream);
+
+/*
+ * mx_quantize_axis / mx_dequantize_axis -- the codec with an explicit block
+ * axis.  Dialect page, section "The block axis": a block's scale must be
+ * constant along the reduction it multiplies, so blocks go on the reduction
+ * axis -- the last axis of A [M, K], axis 0 of a K x N matrix B.
+ *   axis = 1: blocks x[r, 32j .. 32j+31]; identical to mx_quantize /
+ *             mx_dequantize (same layouts, same requirements).
+ *   axis = 0: blocks x[32i .. 32i+31, c] of a row-major [rows, cols] float32
+ *             matrix; rows must be a multiple of 32.  Storage is block-major,
+ *             the layout mx_quantize gives for the transposed matrix:
+ *             codes [cols, rows/2] (E2M1, element 32i+2k of column c in the
+ *             low nibble of byte 16i+k of codes row c) or [cols, rows] (E4M3),
+ *             scales [cols, rows/32].  So mx_quantize_axis(B, axis 0) of a
+ *             K x N matrix B yields the B^T operand of mx_block_matmul.
+ * Per block, the arithmetic is that of mx_quantize / mx_dequantize.
+ * x / y: device float32 [rows, cols], 16-byte aligned; codes 16-byte aligned.
+ * Errors: MX_ERR_UNSUPPORTED for axis not 0 or 1, MX_ERR_SHAPE for rows (axis
+ * 0) or cols (axis 1) not a multiple of 32; otherwise as mx_quantize.
+ */
+mx_status_t mx_quantize_axis(const float *x, void *codes, uint8_t *scales, int64_t rows,
+                             int64_t cols, int32_t axis, mx_elem_t elem, int32_t block_size,
+                             mx_stream_t stream);
+mx_status_t mx_dequantize_axis(const void *codes, const uint8_t *scales, float *y, int64_t rows,
+                               int64_t cols, int32_t axis, mx_elem_t elem, int32_t block_size,
+                               mx_stream_t stream);
+
+/*
+ * mx_fold_scale -- in place, turn the scales of a block-scaled tensor X into
+ * those of 2^j * X; codes are untouched.  Dialect page, section "The four
+ * ops" (fold_scale: a scalar multiply of a block-scaled value folded without
+ * touching its elements, exact for powers of two); "Bit Layout", section
+ * "The E8M0 shared scale" (byte s is 2^(s-127), 0xFF is NaN).
+ * Every scale byte s becomes s + j when s != 0xFF and 0 <= s + j <= 254;
+ * otherwise no E8M0 byte represents the product and the byte becomes 0xFF
+ * (its block decodes to NaN).  Exact or NaN, never silently rounded.
+ * scales: device, n_scales bytes, any alignment (read and written).
+ * Errors: MX_ERR_NULL, MX_ERR_SHAPE for n_scales < 1.
+ */
+mx_status_t mx_fold_scale(uint8_t *scales, int64_t n_scales, int32_t j, mx_stream_t stream);
 
 /* Bytes of the codes of a [rows, cols] tensor: rows*cols/2 (E2M1) or
  * rows*cols (E4M3); 0 for an invalid element type or negative size. */

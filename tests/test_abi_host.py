@@ -33,7 +33,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "mx_abi_version", "mx_block_matmul", "mx_codes_bytes", "mx_dequantize",
-        "mx_num_scale_blocks", "mx_quantize", "mx_status_string"])
+        "mx_dequantize_axis", "mx_fold_scale", "mx_num_scale_blocks", "mx_quantize",
+        "mx_quantize_axis", "mx_status_string"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -42,7 +43,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version(L):
-    assert B.mx_abi_version() == 1
+    assert B.mx_abi_version() == 2
 
 
 def test_size_helpers(L):
@@ -84,6 +85,31 @@ def test_codec_validation(L, args, status):
     assert L.mx_quantize(*args, None) == status
     x, c, s, r, k, e, bs = args
     assert L.mx_dequantize(c, s, x, r, k, e, bs, None) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((X, C, S, 64, 4, 2, 1, 32), 3),        # axis other than 0 / 1
+    ((X, C, S, 64, 4, -1, 1, 32), 3),
+    ((X, C, S, 48, 4, 0, 1, 32), 2),        # axis 0: rows not a multiple of 32
+    ((X, C, S, 64, 0, 0, 1, 32), 2),        # no cols
+    ((X, C, S, 64, 4, 0, 5, 32), 3),        # bad element type
+    ((X, C, S, 64, 4, 0, 1, 8), 3),         # block size other than 32
+    ((0, C, S, 64, 4, 0, 1, 32), 1),        # null x
+    ((X, C, 0, 64, 4, 0, 2, 32), 1),        # null scales
+    ((X + 8, C, S, 64, 4, 0, 1, 32), 4),    # misaligned x
+    ((X, C + 4, S, 64, 4, 0, 1, 32), 4),    # misaligned codes
+    ((X, C, S, 4, 48, 1, 1, 32), 2),        # axis 1: cols not a multiple of 32
+])
+def test_axis_codec_validation(L, args, status):
+    x, c, s, r, k, axis, e, bs = args
+    assert L.mx_quantize_axis(x, c, s, r, k, axis, e, bs, None) == status
+    assert L.mx_dequantize_axis(c, s, x, r, k, axis, e, bs, None) == status
+
+
+def test_fold_scale_validation(L):
+    assert L.mx_fold_scale(0, 16, 3, None) == 1
+    assert L.mx_fold_scale(S, 0, 3, None) == 2
+    assert L.mx_fold_scale(S, -5, 3, None) == 2
 
 
 @pytest.mark.parametrize("over,status", [
