@@ -48,6 +48,8 @@ def lib() -> ctypes.CDLL:
     L.mx_dequantize.restype = i32
     L.mx_block_matmul.argtypes = [p, p, i32, p, p, i32, p, i64, i64, i64, i32, i32, p]
     L.mx_block_matmul.restype = i32
+    L.mx_block_matmul_f32b.argtypes = [p, p, i32, p, p, i64, i64, i64, i32, i32, p]
+    L.mx_block_matmul_f32b.restype = i32
     L.mx_quantize_axis.argtypes = [p, p, p, i64, i64, i32, i32, i32, p]
     L.mx_quantize_axis.restype = i32
     L.mx_dequantize_axis.argtypes = [p, p, p, i64, i64, i32, i32, i32, p]
@@ -100,6 +102,12 @@ def mx_block_matmul(a_codes, a_scales, a_elem, b_codes, b_scales, b_elem, c, M, 
                     block_size=BLOCK, accumulate=0, stream=None):
     _check(lib().mx_block_matmul(a_codes, a_scales, a_elem, b_codes, b_scales, b_elem, c,
                                  M, N, K, block_size, accumulate, stream))
+
+
+def mx_block_matmul_f32b(a_codes, a_scales, a_elem, b, c, M, N, K, block_size=BLOCK,
+                         accumulate=0, stream=None):
+    _check(lib().mx_block_matmul_f32b(a_codes, a_scales, a_elem, b, c, M, N, K, block_size,
+                                      accumulate, stream))
 
 
 def mx_codes_bytes(rows, cols, elem) -> int:
@@ -232,4 +240,27 @@ def block_matmul(a: MXTensor, bt: MXTensor, out=None, accumulate: bool = False):
     mx_block_matmul(a.codes.data_ptr(), a.scales.data_ptr(), a.elem, bt.codes.data_ptr(),
                     bt.scales.data_ptr(), bt.elem, out.data_ptr(), M, N, K, BLOCK,
                     1 if accumulate else 0, _stream_ptr(out.device))
+    return out
+
+
+def block_matmul_f32b(a: MXTensor, b, out=None, accumulate: bool = False):
+    """C = [C +] A . B with A [M, K] block-scaled along K and B an ordinary
+    float32 [K, N] GPU tensor (mx_block_matmul_f32b)."""
+    import torch
+    if a.axis != 1:
+        raise ValueError("A must be blocked along its last axis (K)")
+    _require(b, torch.float32, "b")
+    if b.dim() != 2 or b.shape[0] != a.cols:
+        raise ValueError(f"B must be [K={a.cols}, N], got {tuple(b.shape)}")
+    M, K, N = a.rows, a.cols, b.shape[1]
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs an existing out tensor")
+        out = torch.empty((M, N), dtype=torch.float32, device=b.device)
+    _require(out, torch.float32, "out")
+    _require(a.codes, torch.uint8, "a.codes")
+    _require(a.scales, torch.uint8, "a.scales")
+    mx_block_matmul_f32b(a.codes.data_ptr(), a.scales.data_ptr(), a.elem, b.data_ptr(),
+                         out.data_ptr(), M, N, K, BLOCK, 1 if accumulate else 0,
+                         _stream_ptr(out.device))
     return out

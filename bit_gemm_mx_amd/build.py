@@ -21,7 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmx.so")
 SOURCES = ["libmx.cpp", "quantize.hip", "dequantize.hip", "codec_axis0.hip",
-           "scale_ops.hip", "block_matmul.hip"]
+           "scale_ops.hip", "block_matmul.hip", "block_matmul_f32b.hip"]
 ARCH = "gfx950"
 
 

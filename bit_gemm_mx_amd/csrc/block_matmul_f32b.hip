@@ -1,0 +1,209 @@
+// MX block matmul with an ordinary float32 B: C[M,N] (+)= A[M,K] . B[K,N],
+// A block-scaled along K (codes + E8M0 scales), B row-major float32 [K, N].
+// This is block_matmul as the dialect page "A Dialect Is a Set of
+// Co-Designed Decisions" states its first version (section "The four ops":
+// a block-scaled A of shape MxK, an ordinary f32 B of shape KxN, C += A.B;
+// section "The accumulator operand": C is updated in place).
+//
+// Arithmetic: A's elements are decoded exactly (grid value x 2^(byte-127),
+// codec_common.h) and multiplied with B on the fp32 matrix cores
+// (v_mfma_f32_16x16x4_f32).  Each 32-element block of K is summed into a
+// fresh accumulator P, blocks are summed into G in groups of 16, and groups
+// into T -- each partial sum spans at most 32 products, 16 blocks or K/512
+// groups, so the fp32 rounding error stays near 64 ulp of sum |a b| at
+// K = 8192 instead of growing with K.  A NaN scale byte or E4M3 NaN code makes
+// the outputs of its row NaN.
+//
+// MFMA layout (16x16x4 f32): lane l supplies A[l % 16][l / 16] and
+// B[l / 16][l % 16] of the 16x4 / 4x16 operand step and holds
+// C[4 (l / 16) + r][l % 16], r = 0..3.  Operands come straight from global
+// memory into registers: a lane loads the whole 16/32-byte code block of its
+// A row (the 4 lanes of a row share it through the cache) and 8 of B's rows
+// for its column, 64 contiguous bytes per 16 lanes.  No LDS staging: at the
+// fp32 matrix rate the operand traffic per MFMA is small.
+//
+// Two launch shapes: a 64x64 tile per workgroup (4 waves of 2x2 MFMA tiles,
+// whole K each) when that gives at least one workgroup per CU; otherwise a
+// 16x16 tile per workgroup whose 4 waves split K and add their partial sums
+// in LDS in a fixed order (so results do not depend on timing).
+#include "codec_common.h"
+
+namespace mx {
+namespace {
+
+using namespace codec;
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+
+// Decoded (scaled) A values of K steps s = 0..7 of one block for lane group
+// q: elements k = q + 4s of the block.
+template <int ELEM>
+__device__ __forceinline__ void a_block_values(float (&v)[8], const uint8_t* __restrict__ codes,
+                                               const uint8_t* __restrict__ scales, int64_t row,
+                                               int64_t M, int64_t j, int64_t kb, int q) {
+  if (row >= M) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) v[s] = 0.f;
+    return;
+  }
+  const uint32_t byte = scales[row * kb + j];
+  const float sc = scale_value(byte);
+  if (ELEM == kE2M1) {
+    const u4v w = *reinterpret_cast<const u4v*>(codes + row * (kb * 16) + j * 16);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int k = q + 4 * s;  // nibble k of the 16-byte block
+      v[s] = __uint_as_float(decode_e2m1(w[k >> 3] >> (4 * (k & 7)), sc));
+    }
+  } else {
+    const u4v w0 = *reinterpret_cast<const u4v*>(codes + row * (kb * 32) + j * 32);
+    const u4v w1 = *reinterpret_cast<const u4v*>(codes + row * (kb * 32) + j * 32 + 16);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int k = q + 4 * s;
+      const uint32_t word = k < 16 ? w0[k >> 2] : w1[(k - 16) >> 2];
+      v[s] = __uint_as_float(decode_e4m3((word >> (8 * (k & 3))) & 0xFFu, sc));
+    }
+  }
+  if (byte == 0xFFu) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) v[s] = __uint_as_float(kNaN);
+  }
+}
+
+// B values of K steps s = 0..7 of block j for lane group q and column col.
+__device__ __forceinline__ void b_block_values(float (&v)[8], const float* __restrict__ b,
+                                               int64_t col, int64_t N, int64_t j, int q) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) v[s] = col < N ? b[(32 * j + q + 4 * s) * N + col] : 0.f;
+}
+
+// TI x TJ tiles of 16x16 per wave.  SPLIT = 1: the 4 waves tile the
+// workgroup's (2 TI x 16) x (2 TJ x 16) block of C, each over all of K.
+// SPLIT = 4: the 4 waves share one (TI x 16) x (TJ x 16) block and split K.
+template <int ELEM, int SPLIT, int TI, int TJ>
+__global__ void __launch_bounds__(kThreads)
+block_matmul_f32b_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa,
+                         const float* __restrict__ b, float* __restrict__ c, int64_t M, int64_t N,
+                         int64_t K, int accumulate, int tiles_n) {
+  constexpr int WM = SPLIT == 1 ? 2 : 1, WN = SPLIT == 1 ? 2 : 1;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r16 = lane & 15, q = lane >> 4;
+  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+  const int wm = SPLIT == 1 ? (w >> 1) : 0, wn = SPLIT == 1 ? (w & 1) : 0;
+  const int64_t m0 = (int64_t)tm * (WM * TI * 16) + wm * (TI * 16);
+  const int64_t n0 = (int64_t)tn * (WN * TJ * 16) + wn * (TJ * 16);
+  const int64_t kb = K / 32;
+  const int64_t jb = SPLIT == 1 ? 0 : (kb * w) / SPLIT;
+  const int64_t je = SPLIT == 1 ? kb : (kb * (w + 1)) / SPLIT;
+
+  v4f T[TI][TJ], G[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int t = 0; t < TJ; ++t) T[i][t] = G[i][t] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  float av[TI][8], bv[TJ][8];
+  for (int64_t j = jb; j < je; ++j) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i) a_block_values<ELEM>(av[i], a, sa, m0 + 16 * i + r16, M, j, kb, q);
+#pragma unroll
+    for (int t = 0; t < TJ; ++t) b_block_values(bv[t], b, n0 + 16 * t + r16, N, j, q);
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int t = 0; t < TJ; ++t) {
+        v4f P = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i][0], bv[t][0],
+                                                     v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+        for (int s = 1; s < 8; ++s)
+          P = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i][s], bv[t][s], P, 0, 0, 0);
+        G[i][t] += P;
+      }
+    if (((j - jb) & 15) == 15) {
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int t = 0; t < TJ; ++t) {
+          T[i][t] += G[i][t];
+          G[i][t] = v4f{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int t = 0; t < TJ; ++t) T[i][t] += G[i][t];
+
+  if (SPLIT > 1) {
+    // Partial sums of the 4 K ranges, added in wave order.
+    __shared__ v4f red[SPLIT][TI][TJ][64];
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int t = 0; t < TJ; ++t) red[w][i][t][lane] = T[i][t];
+    __syncthreads();
+    if (w != 0) return;
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int t = 0; t < TJ; ++t) {
+        v4f s = red[0][i][t][lane];
+#pragma unroll
+        for (int x = 1; x < SPLIT; ++x) s += red[x][i][t][lane];
+        T[i][t] = s;
+      }
+  }
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int t = 0; t < TJ; ++t) {
+      const int64_t col = n0 + 16 * t + r16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t row = m0 + 16 * i + 4 * q + r;
+        if (row < M && col < N) {
+          float v = T[i][t][r];
+          if (accumulate) v += c[row * N + col];
+          c[row * N + col] = v;
+        }
+      }
+    }
+}
+
+template <int ELEM, int SPLIT, int TI, int TJ>
+hipError_t launch_shape(const uint8_t* a, const uint8_t* sa, const float* b, float* c, int64_t M,
+                        int64_t N, int64_t K, int accumulate, hipStream_t stream) {
+  constexpr int BM = (SPLIT == 1 ? 2 : 1) * TI * 16, BN = (SPLIT == 1 ? 2 : 1) * TJ * 16;
+  const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  if (tiles_m * tiles_n > 0x7FFFFFFF || tiles_n > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((block_matmul_f32b_kernel<ELEM, SPLIT, TI, TJ>),
+                     dim3((unsigned)(tiles_m * tiles_n)), dim3(kThreads), 0, stream, a, sa, b, c,
+                     M, N, K, accumulate, (int)tiles_n);
+  return hipGetLastError();
+}
+
+template <int ELEM>
+hipError_t launch_elem(const uint8_t* a, const uint8_t* sa, const float* b, float* c, int64_t M,
+                       int64_t N, int64_t K, int accumulate, hipStream_t stream) {
+  const int64_t big_tiles = ((M + 63) / 64) * ((N + 63) / 64);
+  if (big_tiles >= 256)
+    return launch_shape<ELEM, 1, 2, 2>(a, sa, b, c, M, N, K, accumulate, stream);
+  return launch_shape<ELEM, 4, 1, 1>(a, sa, b, c, M, N, K, accumulate, stream);
+}
+
+}  // namespace
+
+hipError_t launch_block_matmul_f32b(const void* a_codes, const uint8_t* a_scales, int a_elem,
+                                    const float* b, float* c, int64_t M, int64_t N, int64_t K,
+                                    int accumulate, hipStream_t stream) {
+  const uint8_t* a = static_cast<const uint8_t*>(a_codes);
+  if (a_elem == kE2M1)
+    return launch_elem<kE2M1>(a, a_scales, b, c, M, N, K, accumulate, stream);
+  return launch_elem<kE4M3>(a, a_scales, b, c, M, N, K, accumulate, stream);
+}
+
+}  // namespace mx

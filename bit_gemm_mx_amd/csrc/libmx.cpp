@@ -65,6 +65,21 @@ mx_status_t mx_block_matmul(const void* a_codes, const uint8_t* a_scales, mx_ele
                                           reinterpret_cast<hipStream_t>(stream)));
 }
 
+mx_status_t mx_block_matmul_f32b(const void* a_codes, const uint8_t* a_scales, mx_elem_t a_elem,
+                                 const float* b, float* c, int64_t M, int64_t N, int64_t K,
+                                 int32_t block_size, int32_t accumulate, mx_stream_t stream) {
+  if (!a_codes || !a_scales || !b || !c) return MX_ERR_NULL;
+  if (!is_elem(a_elem) || block_size != MX_BLOCK_SIZE) return MX_ERR_UNSUPPORTED;
+  if (M < 1 || N < 1 || K < 1 || K % MX_BLOCK_SIZE != 0) return MX_ERR_SHAPE;
+  if (M > INT64_MAX / K || N > INT64_MAX / K || M > INT64_MAX / N) return MX_ERR_SHAPE;
+  if (!aligned16(a_codes) || (reinterpret_cast<uintptr_t>(b) & 3) ||
+      (reinterpret_cast<uintptr_t>(c) & 3))
+    return MX_ERR_ALIGN;
+  return from_hip(mx::launch_block_matmul_f32b(a_codes, a_scales, (int)a_elem, b, c, M, N, K,
+                                               accumulate ? 1 : 0,
+                                               reinterpret_cast<hipStream_t>(stream)));
+}
+
 mx_status_t mx_quantize_axis(const float* x, void* codes, uint8_t* scales, int64_t rows,
                              int64_t cols, int32_t axis, mx_elem_t elem, int32_t block_size,
                              mx_stream_t stream) {

@@ -33,4 +33,9 @@ hipError_t launch_block_matmul(const void* a_codes, const uint8_t* a_scales, int
                                float* c, int64_t M, int64_t N, int64_t K, int accumulate,
                                hipStream_t stream);
 
+// Block-scaled A times float32 B[K, N] (block_matmul_f32b.hip).
+hipError_t launch_block_matmul_f32b(const void* a_codes, const uint8_t* a_scales, int a_elem,
+                                    const float* b, float* c, int64_t M, int64_t N, int64_t K,
+                                    int accumulate, hipStream_t stream);
+
 }  // namespace mx

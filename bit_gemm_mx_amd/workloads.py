@@ -84,3 +84,22 @@ def prefill_linear_case(M: int = 2048, N: int = 28672, K: int = 8192, seed: int 
     a = normal_with_outliers(rng, (M, K), 1.0, 0.005, 20.0)
     bt = rng.standard_normal((N, K), dtype=np.float32) * np.float32(0.02)
     return a, bt
+
+
+def f32b_decode_case(M: int = 4096, N: int = 16, K: int = 4096, seed: int = 1006):
+    """Weight-only quantization, decode-shaped: weights A [M, K] N(0, 0.02)
+    with 0.1% outliers x50 (to be quantized along K) times float32
+    activations B [K, N] N(0, 1)."""
+    rng = np.random.default_rng(seed)
+    a = normal_with_outliers(rng, (M, K), 0.02, 0.001, 50.0)
+    b = rng.standard_normal((K, N), dtype=np.float32)
+    return a, b
+
+
+def f32b_square_case(M: int = 4096, N: int = 4096, K: int = 4096, seed: int = 1007):
+    """Weight-only quantization, square: A [M, K] N(0, 0.02) times float32
+    B [K, N] N(0, 1)."""
+    rng = np.random.default_rng(seed)
+    a = rng.standard_normal((M, K), dtype=np.float32) * np.float32(0.02)
+    b = rng.standard_normal((K, N), dtype=np.float32)
+    return a, b

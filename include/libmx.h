@@ -120,6 +120,25 @@ mx_status_t mx_block_matmul(const void *a_codes, const uint8_t *a_scales, mx_ele
                             int32_t accumulate, mx_stream_t stream);
 
 /*
+ * mx_block_matmul_f32b -- C = [accumulate ? C : 0] + A . B with A block-scaled
+ * and B an ordinary float32 matrix.  This is block_matmul as the dialect
+ * page's first version defines it (section "The four ops": a block-scaled A
+ * of shape MxK, an ordinary f32 B of shape KxN, an accumulator C, C += A.B;
+ * section "The accumulator operand": C is updated in place).
+ *   A: a_codes [M, K or K/2] + a_scales [M, K/32], element type a_elem;
+ *      a_codes 16-byte aligned.
+ *   B: device float32 [K, N], row-major, 4-byte aligned (read).
+ *   C: device float32 [M, N], 4-byte aligned; read only if accumulate != 0.
+ *   C[m,n] = sum_j 2^(sa[m,j]-127) * sum_{k in block j} qa[m,k] * B[k,n]
+ * with float32 products and block-wise float32 sums; a NaN scale or E4M3 NaN
+ * code in row m of A makes row m of C NaN.
+ * Errors as mx_block_matmul (MX_ERR_ALIGN for a misaligned a_codes, b or c).
+ */
+mx_status_t mx_block_matmul_f32b(const void *a_codes, const uint8_t *a_scales, mx_elem_t a_elem,
+                                 const float *b, float *c, int64_t M, int64_t N, int64_t K,
+                                 int32_t block_size, int32_t accumulate, mx_stream_t stream);
+
+/*
  * mx_quantize_axis / mx_dequantize_axis -- the codec with an explicit block
  * axis.  Dialect page, section "The block axis": a block's scale must be
  * constant along the reduction it multiplies, so blocks go on the reduction

@@ -27,12 +27,13 @@ def L():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(mx_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(mx_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
-        "mx_abi_version", "mx_block_matmul", "mx_codes_bytes", "mx_dequantize",
+        "mx_abi_version", "mx_block_matmul", "mx_block_matmul_f32b", "mx_codes_bytes",
+        "mx_dequantize",
         "mx_dequantize_axis", "mx_fold_scale", "mx_num_scale_blocks", "mx_quantize",
         "mx_quantize_axis", "mx_status_string"])
 
@@ -123,6 +124,19 @@ def test_matmul_validation(L, over, status):
     a.update(over)
     assert L.mx_block_matmul(a["a"], a["sa"], a["ae"], a["b"], a["sb"], a["be"], a["c"],
                              a["M"], a["N"], a["K"], a["bs"], a["acc"], None) == status
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(a=0), 1), (dict(sa=0), 1), (dict(b=0), 1), (dict(c=0), 1),
+    (dict(ae=3), 3), (dict(bs=16), 3),
+    (dict(M=0), 2), (dict(N=0), 2), (dict(K=0), 2), (dict(K=48), 2), (dict(N=-1), 2),
+    (dict(a=X + 8), 4), (dict(b=C + 2), 4), (dict(c=Y + 1), 4),
+])
+def test_matmul_f32b_validation(L, over, status):
+    a = dict(a=X, sa=S, ae=2, b=C, c=Y, M=16, N=16, K=128, bs=32, acc=0)
+    a.update(over)
+    assert L.mx_block_matmul_f32b(a["a"], a["sa"], a["ae"], a["b"], a["c"], a["M"], a["N"],
+                                  a["K"], a["bs"], a["acc"], None) == status
 
 
 def test_python_layer_rejects_cpu_tensors(L):

@@ -1,0 +1,157 @@
+"""GPU parity of mx_block_matmul_f32b (block-scaled A times an ordinary
+float32 B) against the oracle.
+
+Bound, per output element: |gpu - oracle| <= 1e-5 * sum_k |a_k b_k|
+(+ |C_in| when accumulating), the matmul tolerance of the quantized path,
+with identical NaN positions and exact zeros where the bound is 0.  Shapes
+cover both launch shapes (16x16 tiles with K split over 4 waves; 64x64
+tiles), ragged M, N and K, and the two measured workloads in full: decode
+(MXFP4 weights 4096x4096 times float32 activations 4096x16) and the square
+4096^3 product.
+"""
+import numpy as np
+import pytest
+import torch
+
+from bit_gemm_mx_amd import binding as B
+from bit_gemm_mx_amd import workloads as W
+from oracle import mx_oracle as O
+
+from gpu_util import assert_matmul_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+ELEMS = [O.E2M1, O.E4M3]
+
+
+def rand_a(rng, M, K, elem, lo=110, hi=145):
+    if elem == O.E2M1:
+        codes = O.pack_nibbles(rng.integers(0, 16, (M, K), dtype=np.uint8))
+    else:
+        el = rng.integers(0, 256, (M, K), dtype=np.uint8)
+        el[(el & 0x7F) == 0x7F] = 0x38
+        codes = el
+    return codes, rng.integers(lo, hi, (M, K // 32), dtype=np.uint8)
+
+
+def rand_b(rng, K, N):
+    b = rng.standard_normal((K, N)).astype(np.float32)
+    return b * np.exp2(rng.integers(-20, 20, (1, N))).astype(np.float32)
+
+
+def run(ac, asc, elem, b, M, N, K, c_in=None, accumulate=False):
+    a = B.MXTensor(dev(ac), dev(asc), M, K, elem)
+    out = dev(c_in.astype(np.float32)) if c_in is not None else None
+    return host(B.block_matmul_f32b(a, dev(b), out=out, accumulate=accumulate))
+
+
+SHAPES = [(1, 1, 32), (3, 5, 64), (16, 16, 128), (17, 33, 160), (70, 100, 1056), (5, 7, 8192),
+          (300, 520, 2048), (1024, 1024, 512), (1030, 1100, 320), (64, 2048, 96)]
+
+
+@pytest.mark.parametrize("elem", ELEMS)
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_random_operands(elem, M, N, K):
+    rng = np.random.default_rng(M * 131 + N * 7 + K + elem)
+    ac, asc = rand_a(rng, M, K, elem)
+    b = rand_b(rng, K, N)
+    got = run(ac, asc, elem, b, M, N, K)
+    want, mag = O.block_matmul_f32b(ac, asc, elem, b, M, N, K)
+    assert_matmul_close(got, want, mag)
+
+
+@pytest.mark.parametrize("elem", ELEMS)
+def test_quantized_float_weights(elem):
+    # weights quantized on the GPU (the usual producer of A), float32 activations
+    rng = np.random.default_rng(3)
+    M, N, K = 200, 48, 2048
+    w = W.normal_with_outliers(rng, (M, K), 0.02, 0.001, 50.0)
+    x = rng.standard_normal((K, N)).astype(np.float32)
+    a = B.quantize(dev(w), elem)
+    got = host(B.block_matmul_f32b(a, dev(x)))
+    ac, asc = O.quantize(w, elem)
+    want, mag = O.block_matmul_f32b(ac, asc, elem, x, M, N, K)
+    assert_matmul_close(got, want, mag)
+
+
+@pytest.mark.parametrize("elem", ELEMS)
+@pytest.mark.parametrize("M,N,K", [(20, 30, 96), (1100, 300, 256)])
+def test_accumulate(elem, M, N, K):
+    rng = np.random.default_rng(M + N + K)
+    ac, asc = rand_a(rng, M, K, elem)
+    b = rand_b(rng, K, N)
+    cin = (rng.standard_normal((M, N)) * 1e5).astype(np.float32)
+    got = run(ac, asc, elem, b, M, N, K, c_in=cin, accumulate=True)
+    want, mag = O.block_matmul_f32b(ac, asc, elem, b, M, N, K, c_in=cin, accumulate=True)
+    assert_matmul_close(got, want, mag)
+
+
+def test_accumulate_zero_does_not_read_c():
+    rng = np.random.default_rng(4)
+    M, N, K = 33, 17, 64
+    ac, asc = rand_a(rng, M, K, O.E2M1)
+    b = rand_b(rng, K, N)
+    got = run(ac, asc, O.E2M1, b, M, N, K, c_in=np.full((M, N), np.nan, np.float32))
+    want, mag = O.block_matmul_f32b(ac, asc, O.E2M1, b, M, N, K)
+    assert_matmul_close(got, want, mag)
+
+
+@pytest.mark.parametrize("elem", ELEMS)
+def test_nan_scales_codes_and_b(elem):
+    rng = np.random.default_rng(5)
+    M, N, K = 40, 36, 256
+    ac, asc = rand_a(rng, M, K, elem)
+    asc[3, 2] = 0xFF
+    if elem == O.E4M3:
+        ac[9, 100] = 0xFF
+    b = rand_b(rng, K, N)
+    b[17, 5] = np.nan
+    got = run(ac, asc, elem, b, M, N, K)
+    want, mag = O.block_matmul_f32b(ac, asc, elem, b, M, N, K)
+    assert np.isnan(want).sum() > 0
+    assert_matmul_close(got, want, mag)
+
+
+def test_zero_rows_and_identity():
+    rng = np.random.default_rng(6)
+    M, K = 48, 64
+    ac, asc = rand_a(rng, M, K, O.E4M3)
+    ac[5] = 0
+    got = run(ac, asc, O.E4M3, np.eye(K, dtype=np.float32), M, K, K)
+    assert np.array_equal(got, O.dequantize(ac, asc, O.E4M3, K))     # -0.0 sums to +0.0
+    assert np.all(got[5] == 0)
+
+
+def test_agrees_with_quantized_b_product():
+    # B holding the dequantized values of a quantized B^T: both entry points
+    # compute the same product
+    rng = np.random.default_rng(7)
+    M, N, K = 300, 260, 1024
+    ac, asc = rand_a(rng, M, K, O.E2M1)
+    bc, bsc = rand_a(rng, N, K, O.E4M3)
+    b = np.ascontiguousarray(O.dequantize(bc, bsc, O.E4M3, K).T)
+    got = run(ac, asc, O.E2M1, b, M, N, K)
+    want, mag = O.block_matmul(ac, asc, O.E2M1, bc, bsc, O.E4M3, M, N, K)
+    assert_matmul_close(got, want, mag)
+
+
+def test_decode_weights_only_full():
+    """MXFP4 weights 4096x4096 times float32 activations 4096x16, every output."""
+    w, x = W.f32b_decode_case()
+    a = B.quantize(dev(w), O.E2M1)
+    got = host(B.block_matmul_f32b(a, dev(x)))
+    ac, asc = host(a.codes), host(a.scales)
+    want, mag = O.block_matmul_f32b(ac, asc, O.E2M1, x, 4096, 16, 4096)
+    assert_matmul_close(got, want, mag)
+
+
+def test_square_4096_full():
+    """MXFP4 A 4096x4096 times float32 B 4096x4096, every output."""
+    w, x = W.f32b_square_case()
+    a = B.quantize(dev(w), O.E2M1)
+    got = host(B.block_matmul_f32b(a, dev(x)))
+    ac, asc = host(a.codes), host(a.scales)
+    del a
+    torch.cuda.empty_cache()
+    want, mag = O.block_matmul_f32b(ac, asc, O.E2M1, x, 4096, 4096, 4096)
+    assert_matmul_close(got, want, mag)
