@@ -11,12 +11,16 @@ rotate over four copies of the workload (4 x 256 MiB of f32, larger than the
 256 MiB Infinity Cache) so that no step reads what the previous one left in
 the caches.
 
-The block-matmul workloads are timed in the same run and reported under
-"parts": the decode-shaped MXFP4 x MXFP4 16x4096x4096 product (HBM-bound),
-the MXFP8 8192^3 product and the prefill linear layer (2048x8192 activations
-quantized on the fly to E4M3, times MXFP4 weights 28672x8192), each with its
-roofline.  Kernel durations come from HIP events recorded on the stream the
-kernels run on.  The CPU oracle is timed on a bounded sample of the step's
+The other workloads are timed in the same run and reported under "parts",
+each with its roofline: the decode-shaped MXFP4 x MXFP4 16x4096x4096 block
+matmul (HBM-bound), the MXFP8 8192^3 product, the prefill linear layer
+(2048x8192 activations quantized on the fly to E4M3, times MXFP4 weights
+28672x8192), the block matmul with an ordinary float32 B (decode-shaped
+4096x4096 MXFP4 weights times 4096x16 activations, and 4096^3), the codec
+with blocks along axis 0 on the 8192x8192 weight workload, and fold_scale on
+its scales.  Kernel durations come from HIP events recorded on the stream the
+kernels run on (for the parts, around replays of a HIP graph of back-to-back
+calls).  The CPU oracle is timed on a bounded sample of the step's
 workload as `cpu_baseline`.
 """
 
@@ -164,21 +168,27 @@ def roofline_hbm(name, k):
 
 
 def timed(torch, name, fn, n):
-    """Average duration of fn over n back-to-back calls between one pair of
-    HIP events on the current stream (and the fastest of three such groups)."""
+    """Average duration of fn over n back-to-back calls (and the fastest of
+    three such groups), from HIP events on the stream the kernels run on.
+
+    The n calls are captured once into a HIP graph and the graph is replayed
+    between the events, so that kernels of a few microseconds are timed back
+    to back on the GPU rather than at the rate the host can launch them."""
     for _ in range(2):
         fn()
     torch.cuda.synchronize()
-    t = EventTimer(torch)
-
-    def group():
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
         for _ in range(n):
             fn()
-
+    g.replay()
+    torch.cuda.synchronize()
+    t = EventTimer(torch)
     for _ in range(3):
-        t.run(name, group)
+        t.run(name, g.replay)
     torch.cuda.synchronize()
     mean, best = t.mean_ms(name)
+    del g
     return mean / n, best / n
 
 
@@ -193,8 +203,8 @@ def hbm_part(ms, mn, byts, extra=None):
     return d
 
 
-def bench_next(mx, W, torch, reps):
-    """The block-axis codec, fold_scale and the f32-B block matmul."""
+def bench_axis0_fold(mx, W, torch, reps):
+    """The codec with blocks along axis 0, and fold_scale."""
     out = {}
     rows = cols = 8192
     # two copies of every buffer, alternated, so that no call reads what the
@@ -221,6 +231,12 @@ def bench_next(mx, W, torch, reps):
     out["fold_scale_8192x8192_scales"] = hbm_part(ms / 2, mn / 2, 2 * qs[0].scales.numel())
     del x0, xs, qs, ys
     progress("axis-0 codec and fold_scale done")
+    return out
+
+
+def bench_f32b(mx, W, torch, reps):
+    """block_matmul with an ordinary float32 B: decode and square workloads."""
+    out = {}
 
     a, b = W.f32b_decode_case()
     at = mx.quantize(torch.from_numpy(a).cuda(), mx.MX_E2M1)
@@ -389,7 +405,8 @@ def main():
     parts = {"codec_kernels": rooflines}
     if not args.no_matmul:
         parts.update(bench_matmuls(mx, W, torch, max(3, args.steps // 2)))
-        parts.update(bench_next(mx, W, torch, max(3, args.steps // 2)))
+        parts.update(bench_f32b(mx, W, torch, max(3, args.steps // 2)))
+    parts.update(bench_axis0_fold(mx, W, torch, max(3, args.steps // 2)))
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),

@@ -78,9 +78,16 @@ quantize_axis0_kernel(const float* __restrict__ x, uint8_t* __restrict__ codes,
   uint8_t* srow = scales + k.ca * nbr;
 
   uint32_t sbytes[kRun / 4] = {};
+  // The run's codes are kept in registers and stored together at the end:
+  // kRun x 16 (E2M1) or 32 (E4M3) contiguous bytes per lane, whole cache
+  // lines, instead of one 16-byte piece of a line per block-row.
+  constexpr int kVecs = kBlockBytes / 16;
+  u4v cbuf[kRun][kVecs];
   float v[32], nv[32];
   load_block(v, x, k.i0, cols, k);
-  for (int r = 0; r < run; ++r) {
+#pragma unroll
+  for (int r = 0; r < kRun; ++r) {
+    if (r >= run) break;  // wave-uniform
     if (r + 1 < run) load_block(nv, x, k.i0 + r + 1, cols, k);
     uint32_t amax = 0, low = 0xFFFFFFFFu;
 #pragma unroll
@@ -112,25 +119,32 @@ quantize_axis0_kernel(const float* __restrict__ x, uint8_t* __restrict__ codes,
 #pragma unroll
       for (int q = 0; q < 8; ++q) w[q] = 0;
     }
-    if (k.live) {
-      const int64_t i = k.i0 + r;
-      if (ELEM == kE2M1) {
-        const u4v d = {w[0] | (w[1] << 16), w[2] | (w[3] << 16), w[4] | (w[5] << 16),
+    if (ELEM == kE2M1) {
+      cbuf[r][0] = u4v{w[0] | (w[1] << 16), w[2] | (w[3] << 16), w[4] | (w[5] << 16),
                        w[6] | (w[7] << 16)};
-        *reinterpret_cast<u4v*>(crow + i * kBlockBytes) = d;
-      } else {
-        const u4v d0 = {w[0], w[1], w[2], w[3]}, d1 = {w[4], w[5], w[6], w[7]};
-        *reinterpret_cast<u4v*>(crow + i * kBlockBytes) = d0;
-        *reinterpret_cast<u4v*>(crow + i * kBlockBytes + 16) = d1;
-      }
+    } else {
+      cbuf[r][0] = u4v{w[0], w[1], w[2], w[3]};
+      cbuf[r][kVecs - 1] = u4v{w[4], w[5], w[6], w[7]};
+    }
+    if (k.live) {
       if (scale_vec)
         sbytes[r >> 2] |= byte << (8 * (r & 3));
       else
-        srow[i] = (uint8_t)byte;
+        srow[k.i0 + r] = (uint8_t)byte;
     }
     if (r + 1 < run) {
 #pragma unroll
       for (int j = 0; j < 32; ++j) v[j] = nv[j];
+    }
+  }
+  if (k.live) {
+#pragma unroll
+    for (int r = 0; r < kRun; ++r) {
+      if (r < run) {
+#pragma unroll
+        for (int h = 0; h < kVecs; ++h)
+          *reinterpret_cast<u4v*>(crow + (k.i0 + r) * kBlockBytes + 16 * h) = cbuf[r][h];
+      }
     }
   }
   // Whole runs with 8-byte aligned scale rows: one store of the run's bytes.
@@ -153,11 +167,22 @@ dequantize_axis0_kernel(const uint8_t* __restrict__ codes, const uint8_t* __rest
 
   uint2 sv = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
   if (scale_vec) sv = *reinterpret_cast<const uint2*>(srow + k.i0);
-  for (int r = 0; r < run; ++r) {
+  // The run's codes, loaded together up front: kRun x 16 or 32 contiguous
+  // bytes per lane, whole cache lines.  Blocks past the run reload the last
+  // block and go unused.
+  constexpr int kVecs = kBlockBytes / 16;
+  u4v cbuf[kRun][kVecs];
+#pragma unroll
+  for (int r = 0; r < kRun; ++r)
+#pragma unroll
+    for (int h = 0; h < kVecs; ++h)
+      cbuf[r][h] = *reinterpret_cast<const u4v*>(crow + (k.i0 + min(r, run - 1)) * kBlockBytes +
+                                                 16 * h);
+#pragma unroll
+  for (int r = 0; r < kRun; ++r) {
+    if (r >= run) break;  // wave-uniform
     const int64_t i = k.i0 + r;
-    u4v d1 = {0, 0, 0, 0};
-    const u4v d0 = *reinterpret_cast<const u4v*>(crow + i * kBlockBytes);
-    if (ELEM == kE4M3) d1 = *reinterpret_cast<const u4v*>(crow + i * kBlockBytes + 16);
+    const u4v d0 = cbuf[r][0], d1 = cbuf[r][kVecs - 1];
     const uint32_t byte =
         scale_vec ? (((r < 4 ? sv.x : sv.y) >> (8 * (r & 3))) & 0xFFu) : srow[i];
     const float s = scale_value(byte);
