@@ -58,8 +58,9 @@ def matmul_bytes(M, N, K, a_bytes, b_bytes, accumulate=False) -> int:
 
 
 def source_hash(*names: str) -> str:
+    """Hash of a kernel's source: its .hip file and the headers it includes."""
     h = hashlib.sha256()
-    for n in names:
+    for n in names + ("codec_common.h", "mx_internal.h"):
         with open(os.path.join(ROOT, "bit_gemm_mx_amd", "csrc", n), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
