@@ -25,7 +25,7 @@ namespace {
 using namespace codec;
 
 constexpr int kThreads = 256;
-constexpr int kRun = 8;  // block-rows per wave
+constexpr int kRun = 4;  // block-rows per wave (measured best of 4, 8, 16)
 
 typedef uint32_t u4v __attribute__((ext_vector_type(4)));
 
@@ -79,8 +79,9 @@ quantize_axis0_kernel(const float* __restrict__ x, uint8_t* __restrict__ codes,
 
   uint32_t sbytes[kRun / 4] = {};
   // The run's codes are kept in registers and stored together at the end:
-  // kRun x 16 (E2M1) or 32 (E4M3) contiguous bytes per lane, whole cache
-  // lines, instead of one 16-byte piece of a line per block-row.
+  // kRun x 16 (E2M1) or 32 (E4M3) contiguous bytes per lane (64 or 128), half
+  // or whole cache lines, instead of one 16-byte piece of a line per
+  // block-row.
   constexpr int kVecs = kBlockBytes / 16;
   u4v cbuf[kRun][kVecs];
   float v[32], nv[32];
@@ -147,9 +148,9 @@ quantize_axis0_kernel(const float* __restrict__ x, uint8_t* __restrict__ codes,
       }
     }
   }
-  // Whole runs with 8-byte aligned scale rows: one store of the run's bytes.
+  // Whole runs with 4-byte aligned scale rows: one store of the run's bytes.
   if (scale_vec && k.live)
-    *reinterpret_cast<uint2*>(srow + k.i0) = make_uint2(sbytes[0], sbytes[1]);
+    *reinterpret_cast<uint32_t*>(srow + k.i0) = sbytes[0];
 }
 
 template <int ELEM>
@@ -165,11 +166,11 @@ dequantize_axis0_kernel(const uint8_t* __restrict__ codes, const uint8_t* __rest
   const uint8_t* crow = codes + k.ca * row_bytes;
   const uint8_t* srow = scales + k.ca * nbr;
 
-  uint2 sv = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
-  if (scale_vec) sv = *reinterpret_cast<const uint2*>(srow + k.i0);
+  uint32_t sv = 0x7F7F7F7Fu;
+  if (scale_vec) sv = *reinterpret_cast<const uint32_t*>(srow + k.i0);
   // The run's codes, loaded together up front: kRun x 16 or 32 contiguous
-  // bytes per lane, whole cache lines.  Blocks past the run reload the last
-  // block and go unused.
+  // bytes per lane, half or whole cache lines.  Blocks past the run reload
+  // the last block and go unused.
   constexpr int kVecs = kBlockBytes / 16;
   u4v cbuf[kRun][kVecs];
 #pragma unroll
@@ -184,7 +185,7 @@ dequantize_axis0_kernel(const uint8_t* __restrict__ codes, const uint8_t* __rest
     const int64_t i = k.i0 + r;
     const u4v d0 = cbuf[r][0], d1 = cbuf[r][kVecs - 1];
     const uint32_t byte =
-        scale_vec ? (((r < 4 ? sv.x : sv.y) >> (8 * (r & 3))) & 0xFFu) : srow[i];
+        scale_vec ? ((sv >> (8 * (r & 3))) & 0xFFu) : srow[i];
     const float s = scale_value(byte);
     uint32_t o[32];
     if (ELEM == kE2M1) {
@@ -223,9 +224,9 @@ Launch plan(const uint8_t* scales, int64_t rows, int64_t cols) {
   Launch l;
   l.grid = dim3((unsigned)((waves + kThreads / 64 - 1) / (kThreads / 64)));
   l.n_runs = n_runs;
-  // Scale runs are stored / loaded as 8 bytes when every run is whole and
-  // every column's scale row starts on an 8-byte boundary.
-  l.scale_vec = (nbr % kRun == 0) && ((reinterpret_cast<uintptr_t>(scales) & 7) == 0);
+  // Scale runs are stored / loaded as 4 bytes when every run is whole and
+  // every column's scale row starts on a 4-byte boundary.
+  l.scale_vec = (nbr % kRun == 0) && ((reinterpret_cast<uintptr_t>(scales) & 3) == 0);
   return l;
 }
 
