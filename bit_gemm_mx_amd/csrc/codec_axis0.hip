@@ -84,12 +84,19 @@ quantize_axis0_kernel(const float* __restrict__ x, uint8_t* __restrict__ codes,
   // block-row.
   constexpr int kVecs = kBlockBytes / 16;
   u4v cbuf[kRun][kVecs];
-  float v[32], nv[32];
-  load_block(v, x, k.i0, cols, k);
+  // Block-rows are loaded kPf ahead of the one being encoded, into a ring of
+  // kPf + 1 register buffers indexed at compile time (measured: one block
+  // ahead 65 us, two 62.5 us, three no better, for the 8192x8192 E2M1 case).
+  constexpr int kPf = 2;
+  float vb[kPf + 1][32];
+#pragma unroll
+  for (int r = 0; r < kPf; ++r)
+    if (r < run) load_block(vb[r], x, k.i0 + r, cols, k);
 #pragma unroll
   for (int r = 0; r < kRun; ++r) {
     if (r >= run) break;  // wave-uniform
-    if (r + 1 < run) load_block(nv, x, k.i0 + r + 1, cols, k);
+    if (r + kPf < run) load_block(vb[(r + kPf) % (kPf + 1)], x, k.i0 + r + kPf, cols, k);
+    const float* v = vb[r % (kPf + 1)];
     uint32_t amax = 0, low = 0xFFFFFFFFu;
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
@@ -132,10 +139,6 @@ quantize_axis0_kernel(const float* __restrict__ x, uint8_t* __restrict__ codes,
         sbytes[r >> 2] |= byte << (8 * (r & 3));
       else
         srow[k.i0 + r] = (uint8_t)byte;
-    }
-    if (r + 1 < run) {
-#pragma unroll
-      for (int j = 0; j < 32; ++j) v[j] = nv[j];
     }
   }
   if (k.live) {
