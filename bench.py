@@ -193,6 +193,52 @@ def timed(torch, name, fn, n):
     return mean / n, best / n
 
 
+def sustained_clock(torch, fn, seconds=2.0):
+    """Median GFX clock (MHz, over samples and XCDs) that `amd-smi metric
+    --clock` reports while fn runs back to back on the GPU for about
+    `seconds`; None when amd-smi is missing or prints nothing usable.  The
+    published peaks assume 2400 MHz."""
+    import shutil
+    import subprocess
+    import threading
+    exe = shutil.which("amd-smi")
+    if exe is None:
+        return None
+    samples, stop = [], threading.Event()
+
+    def sample():
+        while not stop.is_set():
+            try:
+                r = subprocess.run([exe, "metric", "-g", "0", "--clock", "--json"],
+                                   capture_output=True, text=True, timeout=10)
+                data = json.loads(r.stdout)
+                gpu = data["gpu_data"][0] if isinstance(data, dict) else data[0]
+                for name, v in gpu["clock"].items():
+                    if name.startswith("gfx_") and isinstance(v, dict):
+                        samples.append(float(v["clk"]["value"]))
+            except Exception:
+                pass
+            time.sleep(0.05)
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(4):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    th = threading.Thread(target=sample, daemon=True)
+    t_end = time.perf_counter() + seconds
+    th.start()
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            g.replay()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=15)
+    del g
+    return float(np.median(samples)) if samples else None
+
+
 def hbm_part(ms, mn, byts, extra=None):
     gbs = byts / (ms * 1e-3) / 1e9
     d = {"ms": round(ms, 5), "min_ms": round(mn, 5),
@@ -299,6 +345,13 @@ def bench_matmuls(mx, W, torch, reps):
         "ms": round(ms, 4), "min_ms": round(mn, 4), "tflops": round(tf, 1),
         "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_TFLOPS["fp8"],
                      "unit": "TFLOP/s", "frac": round(tf / PEAK_TFLOPS["fp8"], 4)}}
+    # The card is power-limited on this product: report the clock it held and
+    # the fraction of the peak at that clock beside the published-peak one.
+    mhz = sustained_clock(torch, lambda: mx.block_matmul(at, btt, out=c))
+    if mhz:
+        out["mxfp8_8192x8192x8192"]["sustained_clock_mhz"] = round(mhz)
+        out["mxfp8_8192x8192x8192"]["frac_at_sustained_clock"] = round(
+            tf / (PEAK_TFLOPS["fp8"] * mhz / 2400.0), 4)
     del at, btt, c
     torch.cuda.empty_cache()
 
@@ -331,6 +384,29 @@ def bench_matmuls(mx, W, torch, reps):
     del ad, btt, aq, c
     torch.cuda.empty_cache()
     return out
+
+
+def bench_copy(torch, reps):
+    """Achievable-HBM context: a plain device-to-device copy of 1 GiB (read
+    1 GiB, write 1 GiB), two alternating buffer pairs so that no copy reads
+    what the previous one left in the 256 MiB Infinity Cache."""
+    n = 256 * 1024 * 1024
+    src = [torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0) for _ in range(2)]
+    dst = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(2)]
+    k = [0]
+
+    def one():
+        k[0] += 1
+        dst[k[0] & 1].copy_(src[k[0] & 1])
+    ms, mn = timed(torch, "copy", one, reps)
+    byts = 2 * 4 * n
+    gbs = byts / (ms * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"ms": round(ms, 4), "min_ms": round(mn, 4), "bytes": byts, "achieved": round(gbs, 1),
+            "unit": "GB/s", "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "what": "torch device-to-device copy of 1 GiB (read + write), the achievable-HBM "
+                    "context for the codec kernels' fractions"}
 
 
 def cpu_baseline(W, cols=8192, min_seconds=10.0):
@@ -408,6 +484,8 @@ def main():
         parts.update(bench_matmuls(mx, W, torch, max(3, args.steps // 2)))
         parts.update(bench_f32b(mx, W, torch, max(3, args.steps // 2)))
     parts.update(bench_axis0_fold(mx, W, torch, max(3, args.steps // 2)))
+    parts["hbm_copy_context"] = bench_copy(torch, 5)
+    progress("copy context done")
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
