@@ -281,6 +281,29 @@ def bench_axis0_fold(mx, W, torch, reps):
     return out
 
 
+def bench_roundtrip(mx, W, torch, reps):
+    """The 256x1024 MXFP4 round trip (the correctness workload): quantize and
+    dequantize timed apart; at 1.2 MB per op this measures launch latency,
+    not bandwidth."""
+    case = W.roundtrip_case()
+    x = torch.from_numpy(case.x).cuda()
+    rows, cols = x.shape
+    q = mx.empty_mx(rows, cols, mx.MX_E2M1, x.device)
+    y = torch.empty_like(x)
+    byts = codec_bytes(rows, cols, 0.5)
+    ms, mn = timed(torch, "rt_q", lambda: mx.quantize(x, mx.MX_E2M1, out=q), max(reps, 50))
+    out = {"roundtrip_quantize_e2m1_256x1024": hbm_part(ms, mn, byts)}
+    # decoded from a copy whose two chosen blocks carry the NaN scale 0xFF
+    qd = mx.empty_mx(rows, cols, mx.MX_E2M1, x.device)
+    qd.codes.copy_(q.codes)
+    qd.scales.copy_(q.scales)
+    qd.scales.view(-1)[torch.from_numpy(case.ff_blocks).cuda()] = 0xFF
+    ms, mn = timed(torch, "rt_d", lambda: mx.dequantize(qd, out=y), max(reps, 50))
+    out["roundtrip_dequantize_e2m1_256x1024"] = hbm_part(ms, mn, byts)
+    del x, q, qd, y
+    return out
+
+
 def bench_f32b(mx, W, torch, reps):
     """block_matmul with an ordinary float32 B: decode and square workloads."""
     out = {}
@@ -484,6 +507,7 @@ def main():
         parts.update(bench_matmuls(mx, W, torch, max(3, args.steps // 2)))
         parts.update(bench_f32b(mx, W, torch, max(3, args.steps // 2)))
     parts.update(bench_axis0_fold(mx, W, torch, max(3, args.steps // 2)))
+    parts.update(bench_roundtrip(mx, W, torch, max(3, args.steps // 2)))
     parts["hbm_copy_context"] = bench_copy(torch, 5)
     progress("copy context done")
     line = {
