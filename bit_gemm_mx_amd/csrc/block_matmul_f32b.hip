@@ -6,7 +6,7 @@
 // section "The accumulator operand": C is updated in place).
 //
 // Arithmetic: A's elements are decoded exactly (grid value x 2^(byte-127),
-// codec_common.h) and multiplied with B on the fp32 matrix cores
+// by the hardware's scaled converts) and multiplied with B on the fp32 matrix cores
 // (v_mfma_f32_16x16x4_f32).  Each 32-element block of K is summed into a
 // fresh accumulator P, blocks are summed into G in groups of 16, and groups
 // into T -- each partial sum spans at most 32 products, 16 blocks or K/512
@@ -17,11 +17,11 @@
 // MFMA layout (16x16x4 f32): lane l supplies A[l % 16][l / 16] and
 // B[l / 16][l % 16] of the 16x4 / 4x16 operand step and holds
 // C[4 (l / 16) + r][l % 16], r = 0..3.  Operands come straight from global
-// memory into registers: a lane loads the whole 16/32-byte code block of its
-// A row (the 4 lanes of a row share it through the cache) and 8 of B's rows
-// for its column, 64 contiguous bytes per 16 lanes; loads run one batch of
-// blocks ahead of the MFMAs.  No LDS staging: at the fp32 matrix rate the
-// operand traffic per MFMA is small.
+// memory into registers: a lane loads its quarter of the code block of its A
+// row (the 4 lanes of a row read the block's 16 or 32 contiguous bytes) and
+// 8 of B's rows for its column, 64 contiguous bytes per 16 lanes; loads run
+// one batch of blocks ahead of the MFMAs.  No LDS staging: at the fp32 matrix
+// rate the operand traffic per MFMA is small.
 //
 // Two launch shapes: a 64x64 tile per workgroup (4 waves of 2x2 MFMA tiles,
 // whole K each) when that gives at least one workgroup per CU; otherwise a
@@ -40,54 +40,70 @@ typedef uint32_t u4v __attribute__((ext_vector_type(4)));
 
 
 // Raw operand data of one 32-element block of K for one 16-row tile of A and
-// one 16-column tile of B, as loaded: A's code block (16 or 32 bytes) and
-// scale byte for row r16, B's 8 values of K steps s = 0..7 (element q + 4s of
-// the block) for column r16.
-template <int ELEM>
+// one 16-column tile of B, as loaded.  Lane group q (= lane / 16) owns the
+// eight consecutive elements 8q .. 8q+7 of the block: K step s of the MFMA
+// takes element 8q + s from lane group q, for A and for B alike.  So a lane
+// loads one dword (E2M1) or two (E4M3) of its A row's code block and the
+// block's scale byte, and B's rows 8q .. 8q+7 of the block for its column.
 struct RawA {
-  u4v w0, w1;  // w1 used by E4M3 only
+  uint32_t w0, w1;  // w1 used by E4M3 only
   uint32_t byte;
 };
 
 // Loads are issued unconditionally: rows past M and columns past N address
-// the last row / column (their values are discarded), and blocks past the
-// end address the last block, so a batch of loads never sits behind a branch.
+// the last row / column, and blocks past the end address the last block, so
+// a batch of loads never sits behind a branch.  Output row i of an MFMA tile
+// depends only on A row i and output column j only on B column j, so what
+// such lanes load only reaches outputs that are never stored.
 template <int ELEM>
-__device__ __forceinline__ void load_a(RawA<ELEM>& r, const uint8_t* __restrict__ codes,
+__device__ __forceinline__ void load_a(RawA& r, const uint8_t* __restrict__ codes,
                                        const uint8_t* __restrict__ scales, int64_t row, int64_t j,
-                                       int64_t kb) {
+                                       int64_t kb, int q) {
   r.byte = scales[row * kb + j];
   if (ELEM == kE2M1) {
-    r.w0 = *reinterpret_cast<const u4v*>(codes + row * (kb * 16) + j * 16);
+    r.w0 = *reinterpret_cast<const uint32_t*>(codes + row * (kb * 16) + j * 16 + 4 * q);
   } else {
-    r.w0 = *reinterpret_cast<const u4v*>(codes + row * (kb * 32) + j * 32);
-    r.w1 = *reinterpret_cast<const u4v*>(codes + row * (kb * 32) + j * 32 + 16);
+    const uint2 v = *reinterpret_cast<const uint2*>(codes + row * (kb * 32) + j * 32 + 8 * q);
+    r.w0 = v.x;
+    r.w1 = v.y;
   }
 }
 
 __device__ __forceinline__ void load_b(float (&v)[8], const float* __restrict__ b, int64_t col,
                                        int64_t N, int64_t j, int q) {
-  const float* p = b + (32 * j + q) * N + col;
+  const float* p = b + (32 * j + 8 * q) * N + col;
 #pragma unroll
-  for (int s = 0; s < 8; ++s) v[s] = p[4 * s * N];
+  for (int s = 0; s < 8; ++s) v[s] = p[s * N];
 }
 
-// Decoded, scaled A values of K steps s = 0..7 (elements q + 4s of the
-// block); zeros for a row past M, NaN for a 0xFF scale.
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+// Decoded, scaled A values of K steps s = 0..7 (elements 8q + s of the
+// block).  gfx950's scaled converts give code value x 2^(byte-127) exactly
+// for every code and scale byte (checked exhaustively on the hardware,
+// subnormal results and the subnormal scale 2^-127 included); a 0xFF byte is
+// passed as a NaN scale, so the whole block decodes to NaN.
 template <int ELEM>
-__device__ __forceinline__ void decode_a(float (&v)[8], const RawA<ELEM>& r, bool live, int q) {
-  const float sc = scale_value(r.byte);
+__device__ __forceinline__ void decode_a(float (&v)[8], const RawA& r) {
+  const float sc = r.byte == 0xFFu ? __uint_as_float(kNaN) : scale_value(r.byte);
+  if (ELEM == kE2M1) {
+    const v2f p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.w0, sc, 0);
+    const v2f p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.w0, sc, 1);
+    const v2f p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.w0, sc, 2);
+    const v2f p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.w0, sc, 3);
+    v[0] = p0.x; v[1] = p0.y; v[2] = p1.x; v[3] = p1.y;
+    v[4] = p2.x; v[5] = p2.y; v[6] = p3.x; v[7] = p3.y;
+  } else {
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const int k = q + 4 * s;
-    uint32_t bits;
-    if (ELEM == kE2M1) {
-      bits = decode_e2m1(r.w0[k >> 3] >> (4 * (k & 7)), sc);
-    } else {
-      const uint32_t word = k < 16 ? r.w0[k >> 2] : r.w1[(k - 16) >> 2];
-      bits = decode_e4m3((word >> (8 * (k & 3))) & 0xFFu, sc);
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t word = h ? r.w1 : r.w0;
+      const v2f lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(word, sc, false);
+      const v2f hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(word, sc, true);
+      v[4 * h] = lo.x;
+      v[4 * h + 1] = lo.y;
+      v[4 * h + 2] = hi.x;
+      v[4 * h + 3] = hi.y;
     }
-    v[s] = !live ? 0.f : (r.byte == 0xFFu ? __uint_as_float(kNaN) : __uint_as_float(bits));
   }
 }
 
@@ -115,19 +131,10 @@ block_matmul_f32b_kernel(const uint8_t* __restrict__ a, const uint8_t* __restric
   const int64_t je = SPLIT == 1 ? kb : (kb * (w + 1)) / SPLIT;
 
   int64_t arow[TI], bcol[TJ];
-  bool alive[TI], blive[TJ];
 #pragma unroll
-  for (int i = 0; i < TI; ++i) {
-    const int64_t row = m0 + 16 * i + r16;
-    alive[i] = row < M;
-    arow[i] = alive[i] ? row : M - 1;
-  }
+  for (int i = 0; i < TI; ++i) arow[i] = min(m0 + 16 * i + r16, M - 1);
 #pragma unroll
-  for (int t = 0; t < TJ; ++t) {
-    const int64_t col = n0 + 16 * t + r16;
-    blive[t] = col < N;
-    bcol[t] = blive[t] ? col : N - 1;
-  }
+  for (int t = 0; t < TJ; ++t) bcol[t] = min(n0 + 16 * t + r16, N - 1);
 
   v4f T[TI][TJ], G[TI][TJ];
 #pragma unroll
@@ -135,14 +142,14 @@ block_matmul_f32b_kernel(const uint8_t* __restrict__ a, const uint8_t* __restric
 #pragma unroll
     for (int t = 0; t < TJ; ++t) T[i][t] = G[i][t] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  RawA<ELEM> ra[2][U][TI];
+  RawA ra[2][U][TI];
   float rb[2][U][TJ][8];
   auto load_batch = [&](const int slot, int64_t j0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t j = min(j0 + u, je - 1);
 #pragma unroll
-      for (int i = 0; i < TI; ++i) load_a<ELEM>(ra[slot][u][i], a, sa, arow[i], j, kb);
+      for (int i = 0; i < TI; ++i) load_a<ELEM>(ra[slot][u][i], a, sa, arow[i], j, kb, q);
 #pragma unroll
       for (int t = 0; t < TJ; ++t) load_b(rb[slot][u][t], b, bcol[t], N, j, q);
     }
@@ -154,14 +161,12 @@ block_matmul_f32b_kernel(const uint8_t* __restrict__ a, const uint8_t* __restric
       if (j >= je) break;  // wave-uniform
       float av[TI][8];
 #pragma unroll
-      for (int i = 0; i < TI; ++i) decode_a<ELEM>(av[i], ra[slot][u][i], alive[i], q);
+      for (int i = 0; i < TI; ++i) decode_a<ELEM>(av[i], ra[slot][u][i]);
 #pragma unroll
       for (int i = 0; i < TI; ++i)
 #pragma unroll
         for (int t = 0; t < TJ; ++t) {
-          float bv[8];
-#pragma unroll
-          for (int s = 0; s < 8; ++s) bv[s] = blive[t] ? rb[slot][u][t][s] : 0.f;
+          const float* bv = rb[slot][u][t];
           v4f P = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i][0], bv[0],
                                                        v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
@@ -253,7 +258,9 @@ hipError_t launch_elem(const uint8_t* a, const uint8_t* sa, const float* b, floa
   const int64_t big_tiles = ((M + 63) / 64) * ((N + 63) / 64);
   if (big_tiles >= 256)
     return launch_shape<ELEM, 1, 2, 2, 1>(a, sa, b, c, M, N, K, accumulate, stream);
-  return launch_shape<ELEM, 16, 1, 1, 2>(a, sa, b, c, M, N, K, accumulate, stream);
+  // One block per load batch: measured fastest of 1, 2 and 4 (and of 4, 8
+  // and 16 waves) on the 4096x4096 . 4096x16 decode shape.
+  return launch_shape<ELEM, 16, 1, 1, 1>(a, sa, b, c, M, N, K, accumulate, stream);
 }
 
 }  // namespace
