@@ -122,6 +122,35 @@ def test_zero_rows_and_identity():
     assert np.all(got[5] == 0)
 
 
+def exhaustive_a(elem, M, K):
+    """Rows cycling through every scale byte whose decoded values stay finite
+    (E2M1 up to 252: 6 * 2^125; E4M3 up to 246: 448 * 2^119) and, along K,
+    every finite code (E4M3's two NaN codes replaced by zero)."""
+    top = 252 if elem == O.E2M1 else 246
+    scales = (np.arange(M * (K // 32)).reshape(M, K // 32) // (K // 32) % (top + 1)).astype(np.uint8)
+    el = (np.arange(K) % (16 if elem == O.E2M1 else 256)).astype(np.uint8)
+    if elem == O.E4M3:
+        el[(el & 0x7F) == 0x7F] = 0
+    el = np.tile(el, (M, 1))
+    codes = O.pack_nibbles(el) if elem == O.E2M1 else el
+    return codes, scales
+
+
+@pytest.mark.parametrize("elem", ELEMS)
+@pytest.mark.parametrize("M,K", [(256, 256), (1024, 1024)])
+def test_identity_b_decodes_every_code_and_scale_exactly(elem, M, K):
+    """C = A . I is A's exact decode (each output is one product with 1 plus
+    zeros), so this pins the in-register decode -- the hardware's scaled
+    converts -- value for value, for every finite code at every scale byte
+    that keeps it finite, subnormal results included.  256 rows take the
+    K-split launch shape, 1024 the 64x64-tile shape."""
+    ac, asc = exhaustive_a(elem, M, K)
+    got = run(ac, asc, elem, np.eye(K, dtype=np.float32), M, K, K)
+    want = O.dequantize(ac, asc, elem, K)
+    assert not np.isnan(want).any()
+    np.testing.assert_array_equal(got, want)   # values: -0.0 sums to +0.0
+
+
 def test_agrees_with_quantized_b_product():
     # B holding the dequantized values of a quantized B^T: both entry points
     # compute the same product
