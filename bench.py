@@ -194,31 +194,31 @@ def timed(torch, name, fn, n):
 
 
 def sustained_clock(torch, fn, seconds=2.0):
-    """Median GFX clock (MHz, over samples and XCDs) that `amd-smi metric
-    --clock` reports while fn runs back to back on the GPU for about
-    `seconds`; None when amd-smi is missing or prints nothing usable.  The
-    published peaks assume 2400 MHz."""
-    import shutil
-    import subprocess
+    """Median GFX clock (MHz) while fn runs back to back on the GPU for about
+    `seconds`, read every 0.1 s from the driver's pp_dpm_sclk file (the line
+    marked '*' is the current clock; plain file reads, no helper process).
+    The first 0.3 s of samples (clock ramp) are dropped.  None when the file
+    is missing or unreadable.  The published peaks assume 2400 MHz."""
+    import glob
+    import re
     import threading
-    exe = shutil.which("amd-smi")
-    if exe is None:
+    files = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    if len(files) != 1:
         return None
     samples, stop = [], threading.Event()
 
     def sample():
         while not stop.is_set():
             try:
-                r = subprocess.run([exe, "metric", "-g", "0", "--clock", "--json"],
-                                   capture_output=True, text=True, timeout=10)
-                data = json.loads(r.stdout)
-                gpu = data["gpu_data"][0] if isinstance(data, dict) else data[0]
-                for name, v in gpu["clock"].items():
-                    if name.startswith("gfx_") and isinstance(v, dict):
-                        samples.append(float(v["clk"]["value"]))
-            except Exception:
+                with open(files[0]) as f:
+                    for line in f:
+                        if line.rstrip().endswith("*"):
+                            m = re.search(r"(\d+)\s*[Mm][Hh]z", line)
+                            if m:
+                                samples.append(float(m.group(1)))
+            except OSError:
                 pass
-            time.sleep(0.05)
+            time.sleep(0.1)
 
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
@@ -234,9 +234,10 @@ def sustained_clock(torch, fn, seconds=2.0):
             g.replay()
         torch.cuda.synchronize()
     stop.set()
-    th.join(timeout=15)
+    th.join(timeout=5)
     del g
-    return float(np.median(samples)) if samples else None
+    steady = samples[3:]
+    return float(np.median(steady)) if steady else None
 
 
 def hbm_part(ms, mn, byts, extra=None):
