@@ -23,7 +23,7 @@
 // one batch of blocks ahead of the MFMAs.  No LDS staging: at the fp32 matrix
 // rate the operand traffic per MFMA is small.
 //
-// Two launch shapes: a 64x64 tile per workgroup (4 waves of 2x2 MFMA tiles,
+// Two launch shapes: a 128x64 tile per workgroup (4 waves of 4x2 MFMA tiles,
 // whole K each) when that gives at least one workgroup per CU; otherwise a
 // 16x16 tile per workgroup whose 16 waves split K (four waves per SIMD hide
 // each other's load and MFMA latencies) and add their partial sums in LDS in
@@ -255,9 +255,11 @@ hipError_t launch_shape(const uint8_t* a, const uint8_t* sa, const float* b, flo
 template <int ELEM>
 hipError_t launch_elem(const uint8_t* a, const uint8_t* sa, const float* b, float* c, int64_t M,
                        int64_t N, int64_t K, int accumulate, hipStream_t stream) {
-  const int64_t big_tiles = ((M + 63) / 64) * ((N + 63) / 64);
+  // 4x2 MFMA tiles per wave: measured fastest of 1x2, 2x2 (1.76 ms), 2x4, 4x2
+  // (1.40 ms), 4x3, 4x4, 8x1 and 8x2 on the 4096^3 product.
+  const int64_t big_tiles = ((M + 127) / 128) * ((N + 63) / 64);
   if (big_tiles >= 256)
-    return launch_shape<ELEM, 1, 2, 2, 1>(a, sa, b, c, M, N, K, accumulate, stream);
+    return launch_shape<ELEM, 1, 4, 2, 1>(a, sa, b, c, M, N, K, accumulate, stream);
   // One block per load batch: measured fastest of 1, 2 and 4 (and of 4, 8
   // and 16 waves) on the 4096x4096 . 4096x16 decode shape.
   return launch_shape<ELEM, 16, 1, 1, 1>(a, sa, b, c, M, N, K, accumulate, stream);

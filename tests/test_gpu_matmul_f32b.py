@@ -4,7 +4,7 @@ float32 B) against the oracle.
 Bound, per output element: |gpu - oracle| <= 1e-5 * sum_k |a_k b_k|
 (+ |C_in| when accumulating), the matmul tolerance of the quantized path,
 with identical NaN positions and exact zeros where the bound is 0.  Shapes
-cover both launch shapes (16x16 tiles with K split over 4 waves; 64x64
+cover both launch shapes (16x16 tiles with K split over the waves; 128x64
 tiles), ragged M, N and K, and the two measured workloads in full: decode
 (MXFP4 weights 4096x4096 times float32 activations 4096x16) and the square
 4096^3 product.
@@ -46,7 +46,8 @@ def run(ac, asc, elem, b, M, N, K, c_in=None, accumulate=False):
 
 
 SHAPES = [(1, 1, 32), (3, 5, 64), (16, 16, 128), (17, 33, 160), (70, 100, 1056), (5, 7, 8192),
-          (300, 520, 2048), (1024, 1024, 512), (1030, 1100, 320), (64, 2048, 96)]
+          (300, 520, 2048), (1024, 1024, 512), (1030, 1100, 320), (64, 2048, 96),
+          (2100, 1100, 320), (2048, 2048, 1024)]
 
 
 @pytest.mark.parametrize("elem", ELEMS)
@@ -137,13 +138,13 @@ def exhaustive_a(elem, M, K):
 
 
 @pytest.mark.parametrize("elem", ELEMS)
-@pytest.mark.parametrize("M,K", [(256, 256), (1024, 1024)])
+@pytest.mark.parametrize("M,K", [(256, 256), (2048, 1024)])
 def test_identity_b_decodes_every_code_and_scale_exactly(elem, M, K):
     """C = A . I is A's exact decode (each output is one product with 1 plus
     zeros), so this pins the in-register decode -- the hardware's scaled
     converts -- value for value, for every finite code at every scale byte
     that keeps it finite, subnormal results included.  256 rows take the
-    K-split launch shape, 1024 the 64x64-tile shape."""
+    K-split launch shape, 2048 x 1024 the 128x64-tile shape."""
     ac, asc = exhaustive_a(elem, M, K)
     got = run(ac, asc, elem, np.eye(K, dtype=np.float32), M, K, K)
     want = O.dequantize(ac, asc, elem, K)
