@@ -469,8 +469,8 @@ def main():
                          "scales the FETCH_SIZE / WRITE_SIZE counters of a --pmc run")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the MX hot path has no "
-              "multi-GPU mode in this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): the MX hot path is "
+              "measured on a single GPU", file=sys.stderr)
         sys.exit(2)
 
     import torch
