@@ -46,12 +46,16 @@ def rand_operand(rng, rows, K, elem, lo=112, hi=142, nan_codes=False):
 
 # Small and decode-like shapes (one to four 16-row tiles of A, K split over
 # the waves of a workgroup in one or many load batches, K not a multiple of
-# 128, several row panels), and shapes for the 256x256-tile kernel with
-# partial tiles in M and N and partial K groups.
+# 128, several row panels), shapes the 256x256-tile kernel does not take
+# (K not a multiple of 512), and shapes it does take with partial tiles in M
+# and N.
 SHAPES = [(1, 1, 32), (3, 4, 96), (16, 16, 128), (17, 33, 160), (64, 48, 1024),
           (33, 100, 4128), (5, 70, 8192), (2, 17, 65536), (200, 70, 1056),
           (100, 70, 3968), (256, 256, 512), (300, 257, 2080), (257, 300, 1152),
-          (130, 520, 640), (512, 256, 128)]
+          (130, 520, 640), (512, 256, 128),
+          # the tiled kernel (M > 64, K a multiple of 512) with partial tiles in M and N
+          (300, 257, 1024), (257, 520, 2048), (1000, 300, 512), (65, 1000, 1536),
+          (777, 1111, 3072)]
 
 
 def quantized_normal(rng, rows, K, elem, sigma=1.0, outliers=0.01, factor=30.0):
