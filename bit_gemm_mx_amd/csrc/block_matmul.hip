@@ -252,8 +252,6 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kTM = 256, kTN = 256;
-constexpr int kScaleRowBytes = 16;                // scale bytes per row per chunk
-constexpr int kScaleBytes = 2 * 256 * kScaleRowBytes;  // A and B rows of one chunk
 
 template <int ELEM, int TK, int WAVES = 4>
 struct Stage {
@@ -349,7 +347,12 @@ __device__ __forceinline__ v8i read_operand(const uint8_t* lds, int r, int h, in
 // memory operations are outstanding, leaving the other counters alone.
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
-template <int AE, int BE, int TK, int WN>
+// Scale staging.  Chunk mode (K a multiple of 512): one 16-byte slice per row
+// (16 blocks = 512 K) per chunk of stages, in two chunk buffers by parity.
+// Stage mode (K a multiple of 128, DW): one dword per row (the stage's 4
+// blocks) with every stage, stored after the stage's code tiles in the same
+// stage buffer.
+template <int AE, int BE, int TK, int WN, bool DW = false>
 struct Pipe {
   static constexpr int kTK = TK;
   static constexpr int kWaves = 2 * WN;                  // 2 along M, WN along N
@@ -357,15 +360,19 @@ struct Pipe {
   static constexpr int kWaveN = 256 / WN;                // columns of C per wave
   static constexpr int kNQ = kWaveN / 32;                // 32x32 MFMA tiles along N per wave
   static constexpr int kSteps = kTK / 64;                // MFMA K steps per stage
-  static constexpr int kChunkStages = 512 / kTK;         // stages per scale chunk
+  static_assert(!DW || kTK == 128, "stage-mode scales hold one dword (4 blocks) per row");
+  static constexpr int kChunkStages = DW ? 1 : 512 / kTK;  // stages per scale chunk
+  static constexpr int kScaleRowBytes = DW ? 4 : 16;     // scale bytes per row per chunk
+  static constexpr int kScaleBytes = 2 * 256 * kScaleRowBytes;  // A and B^T rows of a chunk
   static constexpr int kAB = Stage<AE, kTK>::kBytes + Stage<BE, kTK>::kBytes;
-  // As many stage buffers (4 or 2) as fit next to two scale chunks in 160 KiB.
-  static constexpr int kStages = 4 * kAB + 2 * kScaleBytes <= 160 * 1024 ? 4 : 2;
+  static constexpr int kBuf = kAB + (DW ? kScaleBytes : 0);    // one stage buffer
+  // As many stage buffers (4 or 2) as fit in 160 KiB (with two scale chunks).
+  static constexpr int kStages = 4 * kBuf + (DW ? 0 : 2 * kScaleBytes) <= 160 * 1024 ? 4 : 2;
   // Stages walked per loop iteration: whole scale chunks of both parities.
-  static constexpr int kUnroll = 2 * kChunkStages;
+  static constexpr int kUnroll = 2 * kChunkStages > kStages ? 2 * kChunkStages : kStages;
   static_assert(kUnroll % kStages == 0, "buffer slots must repeat within the unrolled body");
   static constexpr int kDma = Stage<AE, kTK, kWaves>::kInstr + Stage<BE, kTK, kWaves>::kInstr;
-  // Scale chunk: 512 rows (A then B^T) of 16 bytes, 64 rows per load.
+  // Scale chunk: 512 rows (A then B^T), 64 rows per load.
   static constexpr int kScaleDma = 8 / kWaves;           // per wave and chunk
   // Loads a wave issues along with stage s: its code tiles, plus the scale
   // chunk that starts with it.
@@ -379,25 +386,31 @@ struct Pipe {
   }
 };
 
-template <int AE, int BE, int TK, int WN>
+template <typename F, int... U>
+__device__ __forceinline__ void unroll_seq(F&& f, std::integer_sequence<int, U...>) {
+  (f(std::integral_constant<int, U>{}), ...);
+}
+
+template <int AE, int BE, int TK, int WN, bool DW>
 __global__ void __launch_bounds__(128 * WN)
 block_matmul_tiled(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa,
                    const uint8_t* __restrict__ b, const uint8_t* __restrict__ sb,
                    float* __restrict__ c, int64_t M, int64_t N, int64_t K, int accumulate,
                    int tiles_m, int tiles_n) {
-  using P = Pipe<AE, BE, TK, WN>;
+  using P = Pipe<AE, BE, TK, WN, DW>;
   constexpr int kTK = P::kTK, kChunkStages = P::kChunkStages, kWaves = P::kWaves;
   constexpr int kA = Stage<AE, kTK>::kBytes, kAB = P::kAB, kStages = P::kStages;
-  constexpr int kNQ = P::kNQ;
+  constexpr int kNQ = P::kNQ, kBuf = P::kBuf;
+  constexpr int kScaleRowBytes = P::kScaleRowBytes, kScaleBytes = P::kScaleBytes;
   // One array per buffer, always indexed by a compile-time slot, so that the
   // compiler can tell the direct-to-LDS loads into one buffer from the reads
   // of another and keep the loads in flight.
-  __shared__ __attribute__((aligned(1024))) uint8_t smem0[kAB];
-  __shared__ __attribute__((aligned(1024))) uint8_t smem1[kAB];
-  __shared__ __attribute__((aligned(1024))) uint8_t smem2[kStages > 2 ? kAB : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t smem3[kStages > 3 ? kAB : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t scales0[kScaleBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t scales1[kScaleBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem0[kBuf];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem1[kBuf];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem2[kStages > 2 ? kBuf : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem3[kStages > 3 ? kBuf : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t scales0[DW ? 16 : kScaleBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t scales1[DW ? 16 : kScaleBytes];
 
   // Tile order: the hardware deals workgroups round-robin to the 8 XCDs, so
   // give each XCD a contiguous range of tiles, walked in groups of up to 8
@@ -453,15 +466,20 @@ block_matmul_tiled(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa
     stage_b.load(dst + kA, rb, b_row_bytes, (uint32_t)st * Stage<BE, kTK>::kRowBytes, wave);
     if (st % kChunkStages == 0) {
       const uint32_t kb = (uint32_t)(st / kChunkStages) * kScaleRowBytes;
+      uint8_t* sdst = DW ? dst + kAB : (par ? scales1 : scales0);
 #pragma unroll
       for (int j = 0; j < P::kScaleDma; ++j) {
         const int part = wave * P::kScaleDma + j;  // 64-row part of the 512 rows
         const uint32_t off = kb < kblocks ? (uint32_t)(64 * (part & 3) + lane) * kblocks
                                           : kOutOfRange;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            part < 4 ? rsa : rsb,
-            (__attribute__((address_space(3))) void*)((par ? scales1 : scales0) + part * 1024),
-            16, off, kb, 0, 0);
+        auto* d = (__attribute__((address_space(3))) void*)(sdst + part * 64 * kScaleRowBytes);
+        // Each size is a literal: a size that depends on a template parameter
+        // is checked again when the host pass instantiates the kernel, which
+        // rejects 16 (a gfx950-only size) and silently drops the launch stub.
+        if constexpr (DW)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(part < 4 ? rsa : rsb, d, 4, off, kb, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(part < 4 ? rsa : rsb, d, 16, off, kb, 0, 0);
       }
     }
   };
@@ -490,7 +508,7 @@ block_matmul_tiled(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa
 
     const uint8_t* la = slot(buf);
     const uint8_t* lb = la + kA;
-    const uint8_t* sc = par ? scales1 : scales0;
+    const uint8_t* sc = DW ? la + kAB : (par ? scales1 : scales0);
     // The stage covers blocks [blk0, blk0 + kTK/32) of the chunk.  Read the
     // scale dword holding them, shifted so that byte sel0 + 2h holds this
     // lane's block of K step h (lane group g takes block g of each step).
@@ -536,26 +554,7 @@ block_matmul_tiled(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);              // LDS read
     }
   };
-  for (; it < iters; ++it) {
-    stage(std::integral_constant<int, 0>{});
-    stage(std::integral_constant<int, 1>{});
-    stage(std::integral_constant<int, 2>{});
-    stage(std::integral_constant<int, 3>{});
-    stage(std::integral_constant<int, 4>{});
-    stage(std::integral_constant<int, 5>{});
-    stage(std::integral_constant<int, 6>{});
-    stage(std::integral_constant<int, 7>{});
-    if constexpr (P::kUnroll > 8) {
-      stage(std::integral_constant<int, 8>{});
-      stage(std::integral_constant<int, 9>{});
-      stage(std::integral_constant<int, 10>{});
-      stage(std::integral_constant<int, 11>{});
-      stage(std::integral_constant<int, 12>{});
-      stage(std::integral_constant<int, 13>{});
-      stage(std::integral_constant<int, 14>{});
-      stage(std::integral_constant<int, 15>{});
-    }
-  }
+  for (; it < iters; ++it) unroll_seq(stage, std::make_integer_sequence<int, P::kUnroll>{});
   // No load may still be writing this workgroup's LDS when it exits.
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
@@ -586,15 +585,16 @@ block_matmul_tiled(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa
 // on LDS reads, its loads or the barrier.
 constexpr int kTiledTK = 128, kTiledWN = 4;
 
-template <int AE, int BE>
+template <int AE, int BE, bool DW>
 hipError_t launch_tiled(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
                         float* c, int64_t M, int64_t N, int64_t K, int accumulate,
                         hipStream_t stream) {
   constexpr int TK = kTiledTK, WN = kTiledWN;
   const int64_t tiles_m = (M + kTM - 1) / kTM, tiles_n = (N + kTN - 1) / kTN;
-  hipLaunchKernelGGL((block_matmul_tiled<AE, BE, TK, WN>), dim3((unsigned)(tiles_m * tiles_n)),
-                     dim3(Pipe<AE, BE, TK, WN>::kThreads), 0, stream, a, sa, b, sb, c, M, N, K,
-                     accumulate, (int)tiles_m, (int)tiles_n);
+  hipLaunchKernelGGL((block_matmul_tiled<AE, BE, TK, WN, DW>),
+                     dim3((unsigned)(tiles_m * tiles_n)), dim3(Pipe<AE, BE, TK, WN, DW>::kThreads),
+                     0, stream, a, sa, b, sb, c, M, N, K, accumulate, (int)tiles_m,
+                     (int)tiles_n);
   return hipGetLastError();
 }
 
@@ -628,14 +628,17 @@ hipError_t launch_typed(const uint8_t* a, const uint8_t* sa, const uint8_t* b,
                         const uint8_t* sb, float* c, int64_t M, int64_t N, int64_t K,
                         int accumulate, hipStream_t stream) {
   // The tiled kernel addresses a 256-row slab of either operand with 32-bit
-  // buffer offsets, and stages scales as aligned 16-byte row slices (16
-  // blocks), so it needs K % 512 == 0 and 16-byte aligned scale arrays.
+  // buffer offsets, and stages scales either as aligned 16-byte row slices
+  // (16 blocks; K % 512 == 0, 16-byte aligned scale arrays) or as one dword
+  // per row and 128-K stage (K % 128 == 0, 4-byte aligned scale arrays).
   const int64_t slab_a = 256 * (AE == kE2M1 ? K / 2 : K), slab_b = 256 * (BE == kE2M1 ? K / 2 : K);
-  const bool scale_slices = (K % 512 == 0) && ((reinterpret_cast<uintptr_t>(sa) & 15) == 0) &&
-                            ((reinterpret_cast<uintptr_t>(sb) & 15) == 0);
-  if (M > 64 && scale_slices && slab_a < (1ll << 31) && slab_b < (1ll << 31) &&
-      M * (K / 32) < (1ll << 31) && N * (K / 32) < (1ll << 31))
-    return launch_tiled<AE, BE>(a, sa, b, sb, c, M, N, K, accumulate, stream);
+  const uintptr_t align = reinterpret_cast<uintptr_t>(sa) | reinterpret_cast<uintptr_t>(sb);
+  const bool tiled = M > 64 && slab_a < (1ll << 31) && slab_b < (1ll << 31) &&
+                     M * (K / 32) < (1ll << 31) && N * (K / 32) < (1ll << 31);
+  if (tiled && K % 512 == 0 && (align & 15) == 0)
+    return launch_tiled<AE, BE, false>(a, sa, b, sb, c, M, N, K, accumulate, stream);
+  if (tiled && K % 128 == 0 && (align & 3) == 0)
+    return launch_tiled<AE, BE, true>(a, sa, b, sb, c, M, N, K, accumulate, stream);
   return launch_skinny<AE, BE>(a, sa, b, sb, c, M, N, K, accumulate, stream);
 }
 

@@ -113,6 +113,9 @@ mx_status_t mx_dequantize(const void *codes, const uint8_t *scales, float *y, in
  *   C[m,n] = sum_j 2^(sa[m,j]+sb[n,j]-254) * sum_{k in block j} qa[m,k]*qb[n,k]
  * with float32 accumulation; a NaN scale or E4M3 NaN code in row m of A or
  * row n of B^T makes C[m,n] NaN.  Any (a_elem, b_elem) pair of E2M1/E4M3.
+ * Scale arrays may have any alignment; the fastest kernel wants both 16-byte
+ * aligned with K a multiple of 512, or 4-byte aligned with K a multiple of
+ * 128 (other cases take a slower kernel with the same error bound).
  */
 mx_status_t mx_block_matmul(const void *a_codes, const uint8_t *a_scales, mx_elem_t a_elem,
                             const void *b_codes, const uint8_t *b_scales, mx_elem_t b_elem,

@@ -47,7 +47,7 @@ def rand_operand(rng, rows, K, elem, lo=112, hi=142, nan_codes=False):
 # Small and decode-like shapes (one to four 16-row tiles of A, K split over
 # the waves of a workgroup in one or many load batches, K not a multiple of
 # 128, several row panels), shapes the 256x256-tile kernel does not take
-# (K not a multiple of 512), and shapes it does take with partial tiles in M
+# (K not a multiple of 128), and shapes it does take with partial tiles in M
 # and N.
 SHAPES = [(1, 1, 32), (3, 4, 96), (16, 16, 128), (17, 33, 160), (64, 48, 1024),
           (33, 100, 4128), (5, 70, 8192), (2, 17, 65536), (200, 70, 1056),
@@ -55,7 +55,9 @@ SHAPES = [(1, 1, 32), (3, 4, 96), (16, 16, 128), (17, 33, 160), (64, 48, 1024),
           (130, 520, 640), (512, 256, 128),
           # the tiled kernel (M > 64, K a multiple of 512) with partial tiles in M and N
           (300, 257, 1024), (257, 520, 2048), (1000, 300, 512), (65, 1000, 1536),
-          (777, 1111, 3072)]
+          (777, 1111, 3072),
+          # the tiled kernel with per-stage scales (K a multiple of 128 but not of 512)
+          (300, 257, 640), (1000, 300, 384), (65, 700, 1408), (513, 257, 2944)]
 
 
 def quantized_normal(rng, rows, K, elem, sigma=1.0, outliers=0.01, factor=30.0):
@@ -184,6 +186,42 @@ def test_quantized_float_inputs_end_to_end():
     got = host(B.block_matmul(at, btt))
     want, mag = O.block_matmul(oac, oas, O.E4M3, obc, obs, O.E2M1, M, N, K)
     assert_matmul_close(got, want, mag)
+
+
+@pytest.mark.parametrize("offset", [0, 4, 1])
+def test_scale_array_alignment(offset):
+    """Scale arrays at a 16-byte boundary (16-byte scale slices), 4 bytes
+    past one (dword scales per stage) and 1 byte past one (the skinny
+    kernel): all within the tolerance, K a multiple of 512."""
+    rng = np.random.default_rng(90 + offset)
+    M, N, K = 300, 257, 1024
+    ac, asc = quantized_normal(rng, M, K, O.E2M1)
+    bc, bsc = quantized_normal(rng, N, K, O.E2M1, sigma=0.02)
+
+    def shifted(arr):
+        buf = torch.zeros(arr.size + offset, dtype=torch.uint8, device="cuda")
+        view = buf[offset:].view(arr.shape)
+        view.copy_(torch.from_numpy(arr))
+        assert view.data_ptr() % 16 == offset
+        return view
+
+    a = B.MXTensor(dev(ac), shifted(asc), M, K, O.E2M1)
+    b = B.MXTensor(dev(bc), shifted(bsc), N, K, O.E2M1)
+    got = host(B.block_matmul(a, b))
+    want, mag = O.block_matmul(ac, asc, O.E2M1, bc, bsc, O.E2M1, M, N, K)
+    assert_matmul_close(got, want, mag)
+
+
+def test_mlp_down_projection_k11008():
+    """K = 11008 (a multiple of 128, not of 512: per-stage scales in the tiled
+    kernel), E4M3 activations x E2M1 weights, every output."""
+    rng = np.random.default_rng(82)
+    M, N, K = 512, 1024, 11008
+    ac, asc = quantized_normal(rng, M, K, O.E4M3)
+    bc, bsc = quantized_normal(rng, N, K, O.E2M1, sigma=0.02)
+    got = gpu_matmul(ac, asc, O.E4M3, bc, bsc, O.E2M1, M, N, K)
+    want, mag = O.block_matmul(ac, asc, O.E4M3, bc, bsc, O.E2M1, M, N, K)
+    assert_t2(got, want, mag, ac, asc, O.E4M3, bc, bsc, O.E2M1, K)
 
 
 def test_decode_shaped_full():
