@@ -22,7 +22,9 @@
 //     32x32x64 -> C[8(j/4) + 4g + (j%4)][l % 32], j = 0..15.
 // B^T rows use the same layout as A rows (B column n = B^T row n).  A 0xFF
 // scale or an E4M3 NaN code makes the affected outputs NaN in hardware.
+#include <atomic>
 #include <type_traits>
+#include <utility>
 
 #include "mx_internal.h"
 
@@ -236,8 +238,9 @@ block_matmul_skinny(const uint8_t* __restrict__ a, const uint8_t* __restrict__ s
 }
 
 // ---------------------------------------------------------------------------
-// Tiled kernel: 256x256 output tile per workgroup of 2 x WN waves, each wave
-// 128 x (256 / WN) = 4 x (8 / WN) tiles of the 32x32x64 scaled MFMA.
+// Tiled kernel: 256 x TN output tile (TN = 256, or 128 for a last round of
+// tiles) per workgroup of 2 x WN waves, each wave 128 x (TN / WN) = 4 x
+// (TN / 32 / WN) tiles of the 32x32x64 scaled MFMA.
 //
 // K runs in stages of TK elements (TK / 64 MFMA K steps).  Code tiles are
 // staged straight into LDS by buffer loads that write LDS, two or four stage
@@ -251,15 +254,16 @@ block_matmul_skinny(const uint8_t* __restrict__ a, const uint8_t* __restrict__ s
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int kTM = 256, kTN = 256;
+constexpr int kTM = 256;
 
-template <int ELEM, int TK, int WAVES = 4>
+template <int ELEM, int TK, int WAVES = 4, int ROWS = 256>
 struct Stage {
   static constexpr int kRowBytes = ELEM == kE2M1 ? TK / 2 : TK;     // 32 .. 128
   static constexpr int kChunks = kRowBytes / 16;                     // 16-B chunks per row
   static constexpr int kRowsPerLine = 256 / kRowBytes;               // rows per 256-B line
-  static constexpr int kBytes = 256 * kRowBytes;                     // one 256-row tile
+  static constexpr int kBytes = ROWS * kRowBytes;                    // one ROWS-row tile
   static constexpr int kInstr = kBytes / 1024 / WAVES;               // 1-KiB loads per wave
+  static_assert(kInstr * 1024 * WAVES == kBytes, "whole 1-KiB loads per wave");
 };
 
 // LDS byte offset of 16-byte chunk c of row r of a staged tile.  Rows are
@@ -285,16 +289,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 
 constexpr uint32_t kOutOfRange = 0x80000000u;  // past every resource used here
 
-// Stage one 256-row tile of codes straight into LDS with buffer loads that
+// Stage one ROWS-row tile of codes straight into LDS with buffer loads that
 // write LDS directly (each wave instruction fills 1 KiB = 4 lines: lane i
 // writes bytes [16i, 16i+16) of it).  LDS position (line L, chunk p) must hold
 // logical chunk q = p ^ (L % kChunks) of row L * kRowsPerLine + q / kChunks, so
 // each lane fetches that chunk from global memory.  Lane i covers line
 // 4j + i/16 of instruction j; L % kChunks depends on the lane and, for 8 chunks
 // per row, on the parity of j, so two lane offsets are kept.
-template <int ELEM, int TK, int WAVES>
+template <int ELEM, int TK, int WAVES, int ROWS = 256>
 struct Stager {
-  using S = Stage<ELEM, TK, WAVES>;
+  using S = Stage<ELEM, TK, WAVES, ROWS>;
   uint32_t lane_off[2];  // row-in-instruction * row_bytes + 16 * chunk (even / odd j)
   uint32_t chunk16[2];   // 16 * chunk
   uint32_t instr_step;   // bytes between consecutive instructions' first rows
@@ -352,26 +356,28 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4)
 // Stage mode (K a multiple of 128, DW): one dword per row (the stage's 4
 // blocks) with every stage, stored after the stage's code tiles in the same
 // stage buffer.
-template <int AE, int BE, int TK, int WN, bool DW = false>
+template <int AE, int BE, int TK, int WN, bool DW, int TN>
 struct Pipe {
   static constexpr int kTK = TK;
   static constexpr int kWaves = 2 * WN;                  // 2 along M, WN along N
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr int kWaveN = 256 / WN;                // columns of C per wave
+  static constexpr int kWaveN = TN / WN;                 // columns of C per wave
   static constexpr int kNQ = kWaveN / 32;                // 32x32 MFMA tiles along N per wave
+  static_assert(kNQ >= 1 && kNQ * 32 * WN == TN, "whole 32-column MFMA tiles per wave");
   static constexpr int kSteps = kTK / 64;                // MFMA K steps per stage
   static_assert(!DW || kTK == 128, "stage-mode scales hold one dword (4 blocks) per row");
   static constexpr int kChunkStages = DW ? 1 : 512 / kTK;  // stages per scale chunk
   static constexpr int kScaleRowBytes = DW ? 4 : 16;     // scale bytes per row per chunk
   static constexpr int kScaleBytes = 2 * 256 * kScaleRowBytes;  // A and B^T rows of a chunk
-  static constexpr int kAB = Stage<AE, kTK>::kBytes + Stage<BE, kTK>::kBytes;
+  static constexpr int kAB = Stage<AE, kTK>::kBytes + Stage<BE, kTK, 4, TN>::kBytes;
   static constexpr int kBuf = kAB + (DW ? kScaleBytes : 0);    // one stage buffer
   // As many stage buffers (4 or 2) as fit in 160 KiB (with two scale chunks).
   static constexpr int kStages = 4 * kBuf + (DW ? 0 : 2 * kScaleBytes) <= 160 * 1024 ? 4 : 2;
   // Stages walked per loop iteration: whole scale chunks of both parities.
   static constexpr int kUnroll = 2 * kChunkStages > kStages ? 2 * kChunkStages : kStages;
   static_assert(kUnroll % kStages == 0, "buffer slots must repeat within the unrolled body");
-  static constexpr int kDma = Stage<AE, kTK, kWaves>::kInstr + Stage<BE, kTK, kWaves>::kInstr;
+  static constexpr int kDma =
+      Stage<AE, kTK, kWaves>::kInstr + Stage<BE, kTK, kWaves, TN>::kInstr;
   // Scale chunk: 512 rows (A then B^T), 64 rows per load.
   static constexpr int kScaleDma = 8 / kWaves;           // per wave and chunk
   // Loads a wave issues along with stage s: its code tiles, plus the scale
@@ -391,13 +397,13 @@ __device__ __forceinline__ void unroll_seq(F&& f, std::integer_sequence<int, U..
   (f(std::integral_constant<int, U>{}), ...);
 }
 
-template <int AE, int BE, int TK, int WN, bool DW>
+template <int AE, int BE, int TK, int WN, bool DW, int TN>
 __global__ void __launch_bounds__(128 * WN)
 block_matmul_tiled(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa,
                    const uint8_t* __restrict__ b, const uint8_t* __restrict__ sb,
-                   float* __restrict__ c, int64_t M, int64_t N, int64_t K, int accumulate,
-                   int tiles_m, int tiles_n) {
-  using P = Pipe<AE, BE, TK, WN, DW>;
+                   float* __restrict__ c, int64_t M, int64_t N, int64_t K, int64_t ldc,
+                   int accumulate, int tiles_m, int tiles_n) {
+  using P = Pipe<AE, BE, TK, WN, DW, TN>;
   constexpr int kTK = P::kTK, kChunkStages = P::kChunkStages, kWaves = P::kWaves;
   constexpr int kA = Stage<AE, kTK>::kBytes, kAB = P::kAB, kStages = P::kStages;
   constexpr int kNQ = P::kNQ, kBuf = P::kBuf;
@@ -425,7 +431,7 @@ block_matmul_tiled(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa
   const int gsize = min(tiles_m - first_m, kGroup);
   const int tm = first_m + (pid % in_group) % gsize;
   const int tn = (pid % in_group) / gsize;
-  const int64_t m0 = (int64_t)tm * kTM, n0 = (int64_t)tn * kTN;
+  const int64_t m0 = (int64_t)tm * kTM, n0 = (int64_t)tn * TN;
 
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -434,9 +440,9 @@ block_matmul_tiled(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa
   const uint32_t a_row_bytes = AE == kE2M1 ? Ku / 2 : Ku;
   const uint32_t b_row_bytes = BE == kE2M1 ? Ku / 2 : Ku;
   const Stager<AE, kTK, kWaves> stage_a(a_row_bytes, lane);
-  const Stager<BE, kTK, kWaves> stage_b(b_row_bytes, lane);
+  const Stager<BE, kTK, kWaves, TN> stage_b(b_row_bytes, lane);
   const uint32_t kblocks = Ku / 32;
-  const int64_t rows_a = min(M - m0, (int64_t)kTM), rows_b = min(N - n0, (int64_t)kTN);
+  const int64_t rows_a = min(M - m0, (int64_t)kTM), rows_b = min(N - n0, (int64_t)TN);
   // (a 256-row slab of either operand is below 2^31 bytes: checked at launch)
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(a + m0 * a_row_bytes, rows_a * a_row_bytes);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(b + n0 * b_row_bytes, rows_b * b_row_bytes);
@@ -573,8 +579,8 @@ block_matmul_tiled(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa
         const int64_t row = m0 + wm * 128 + 32 * i + 8 * (e >> 2) + 4 * g + (e & 3);
         if (row < M && col < N) {
           float v = acc[i][q][e];
-          if (accumulate) v += c[row * N + col];
-          __builtin_nontemporal_store(v, c + row * N + col);
+          if (accumulate) v += c[row * ldc + col];
+          __builtin_nontemporal_store(v, c + row * ldc + col);
         }
       }
     }
@@ -582,20 +588,62 @@ block_matmul_tiled(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa
 
 // Launch configuration: 128-element K stages, 8 waves (2 x 4, 128 x 64 of C
 // each).  Two waves per SIMD let one wave's MFMAs run while the other waits
-// on LDS reads, its loads or the barrier.
-constexpr int kTiledTK = 128, kTiledWN = 4;
+// on LDS reads, its loads or the barrier.  The 256 x 128 tiles use 4 waves
+// (2 x 2) of the same 128 x 64 shape: 8 waves of 128 x 32 spill registers.
+constexpr int kTiledTK = 128, kTiledWN = 4, kHalfWN = 2;
 
-template <int AE, int BE, bool DW>
+template <int AE, int BE, bool DW, int TN, int WN>
 hipError_t launch_tiled(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
-                        float* c, int64_t M, int64_t N, int64_t K, int accumulate,
+                        float* c, int64_t M, int64_t N, int64_t K, int64_t ldc, int accumulate,
                         hipStream_t stream) {
-  constexpr int TK = kTiledTK, WN = kTiledWN;
-  const int64_t tiles_m = (M + kTM - 1) / kTM, tiles_n = (N + kTN - 1) / kTN;
-  hipLaunchKernelGGL((block_matmul_tiled<AE, BE, TK, WN, DW>),
-                     dim3((unsigned)(tiles_m * tiles_n)), dim3(Pipe<AE, BE, TK, WN, DW>::kThreads),
-                     0, stream, a, sa, b, sb, c, M, N, K, accumulate, (int)tiles_m,
-                     (int)tiles_n);
+  constexpr int TK = kTiledTK;
+  const int64_t tiles_m = (M + kTM - 1) / kTM, tiles_n = (N + TN - 1) / TN;
+  hipLaunchKernelGGL((block_matmul_tiled<AE, BE, TK, WN, DW, TN>),
+                     dim3((unsigned)(tiles_m * tiles_n)),
+                     dim3(Pipe<AE, BE, TK, WN, DW, TN>::kThreads), 0, stream, a, sa, b, sb, c, M,
+                     N, K, ldc, accumulate, (int)tiles_m, (int)tiles_n);
   return hipGetLastError();
+}
+
+// Compute units of the current device (cached per device).
+int cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// One workgroup per compute unit at a time, so 256x256 tiles run in rounds
+// of one tile per CU.  When the last round is at most half full (the
+// 2048 x 28672 prefill product: 896 tiles = 3.5 rounds of 256 CUs), the tile
+// columns holding it are computed by a second launch of 256x128 tiles, which
+// fills the CUs in one round of half-size tiles; the rest of C is one launch
+// of whole rounds.  The two launches write disjoint columns of C.
+template <int AE, int BE, bool DW>
+hipError_t launch_tiled_split(const uint8_t* a, const uint8_t* sa, const uint8_t* b,
+                              const uint8_t* sb, float* c, int64_t M, int64_t N, int64_t K,
+                              int accumulate, hipStream_t stream) {
+  const int64_t tiles_m = (M + kTM - 1) / kTM, tiles_n = (N + 255) / 256;
+  const int64_t tiles = tiles_m * tiles_n, cus = cu_count();
+  const int64_t rem = tiles % cus;
+  const int64_t tail_cols = (rem + tiles_m - 1) / tiles_m;  // tile columns of the last round
+  if (tiles > cus && rem != 0 && tail_cols < tiles_n && 2 * tiles_m * tail_cols <= cus) {
+    const int64_t n1 = (tiles_n - tail_cols) * 256;
+    const int64_t b_row_bytes = BE == kE2M1 ? K / 2 : K;
+    const hipError_t e =
+        launch_tiled<AE, BE, DW, 256, kTiledWN>(a, sa, b, sb, c, M, n1, K, N, accumulate, stream);
+    if (e != hipSuccess) return e;
+    return launch_tiled<AE, BE, DW, 128, kHalfWN>(a, sa, b + n1 * b_row_bytes, sb + n1 * (K / 32),
+                                         c + n1, M, N - n1, K, N, accumulate, stream);
+  }
+  return launch_tiled<AE, BE, DW, 256, kTiledWN>(a, sa, b, sb, c, M, N, K, N, accumulate, stream);
 }
 
 template <int AE, int BE>
@@ -636,9 +684,9 @@ hipError_t launch_typed(const uint8_t* a, const uint8_t* sa, const uint8_t* b,
   const bool tiled = M > 64 && slab_a < (1ll << 31) && slab_b < (1ll << 31) &&
                      M * (K / 32) < (1ll << 31) && N * (K / 32) < (1ll << 31);
   if (tiled && K % 512 == 0 && (align & 15) == 0)
-    return launch_tiled<AE, BE, false>(a, sa, b, sb, c, M, N, K, accumulate, stream);
+    return launch_tiled_split<AE, BE, false>(a, sa, b, sb, c, M, N, K, accumulate, stream);
   if (tiled && K % 128 == 0 && (align & 3) == 0)
-    return launch_tiled<AE, BE, true>(a, sa, b, sb, c, M, N, K, accumulate, stream);
+    return launch_tiled_split<AE, BE, true>(a, sa, b, sb, c, M, N, K, accumulate, stream);
   return launch_skinny<AE, BE>(a, sa, b, sb, c, M, N, K, accumulate, stream);
 }
 
