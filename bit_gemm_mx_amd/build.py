@@ -11,6 +11,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -41,12 +42,34 @@ def common_flags() -> list[str]:
     ]
 
 
+def _scratch_kernels(remarks: str) -> list[str]:
+    """Kernels whose resource-usage remarks report private (scratch) memory."""
+    bad, name = [], None
+    for line in remarks.splitlines():
+        m = re.search(r"remark:\s+Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"remark:\s+ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name and int(m.group(1)) > 0:
+            bad.append(f"{name} ({m.group(1)} bytes/lane)")
+    return bad
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *common_flags(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *common_flags(), "-Rpass-analysis=kernel-resource-usage", "-x", "hip", "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    # No kernel may spill: the tiled matmul counts its outstanding loads by
+    # hand (s_waitcnt vmcnt), and scratch loads and stores would join that
+    # count and release LDS reads before their data has landed.
+    bad = _scratch_kernels(r.stderr)
+    if bad:
+        os.remove(obj)
+        raise RuntimeError(f"{src}: kernels use scratch memory (register spills): {bad}")
     return obj
 
 

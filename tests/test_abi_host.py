@@ -143,3 +143,19 @@ def test_python_layer_rejects_cpu_tensors(L):
     import torch
     with pytest.raises(ValueError):
         B.quantize(torch.zeros(4, 64))
+
+
+def test_build_rejects_kernels_that_spill():
+    """The build parses the compiler's resource-usage remarks and names every
+    kernel with scratch memory (the tiled matmul's hand-counted load waits
+    are only valid without spills)."""
+    from bit_gemm_mx_amd import build
+    remarks = "\n".join([
+        "a.hip:1:1: remark: Function Name: k_ok [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:9:1: remark: Function Name: k_spill [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:9:1: remark:     VGPRs Spill: 12 [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:9:1: remark:     ScratchSize [bytes/lane]: 48 [-Rpass-analysis=kernel-resource-usage]",
+    ])
+    assert build._scratch_kernels(remarks) == ["k_spill (48 bytes/lane)"]
+    assert build._scratch_kernels("") == []
