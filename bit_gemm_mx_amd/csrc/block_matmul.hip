@@ -238,9 +238,9 @@ block_matmul_skinny(const uint8_t* __restrict__ a, const uint8_t* __restrict__ s
 }
 
 // ---------------------------------------------------------------------------
-// Tiled kernel: 256 x TN output tile (TN = 256, or 128 for a last round of
-// tiles) per workgroup of 2 x WN waves, each wave 128 x (TN / WN) = 4 x
-// (TN / 32 / WN) tiles of the 32x32x64 scaled MFMA.
+// Tiled kernel: TM x TN output tile (256 x 256, or 128 x 256 for a last
+// round of tiles) per workgroup of (TM / 128) x WN waves, each wave
+// 128 x (TN / WN) = 4 x (TN / 32 / WN) tiles of the 32x32x64 scaled MFMA.
 //
 // K runs in stages of TK elements (TK / 64 MFMA K steps).  Code tiles are
 // staged straight into LDS by buffer loads that write LDS, two or four stage
@@ -254,7 +254,6 @@ block_matmul_skinny(const uint8_t* __restrict__ a, const uint8_t* __restrict__ s
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int kTM = 256;
 
 template <int ELEM, int TK, int WAVES = 4, int ROWS = 256>
 struct Stage {
@@ -356,10 +355,10 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4)
 // Stage mode (K a multiple of 128, DW): one dword per row (the stage's 4
 // blocks) with every stage, stored after the stage's code tiles in the same
 // stage buffer.
-template <int AE, int BE, int TK, int WN, bool DW, int TN>
+template <int AE, int BE, int TK, int WN, bool DW, int TM, int TN>
 struct Pipe {
   static constexpr int kTK = TK;
-  static constexpr int kWaves = 2 * WN;                  // 2 along M, WN along N
+  static constexpr int kWaves = TM / 128 * WN;           // TM / 128 along M, WN along N
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int kWaveN = TN / WN;                 // columns of C per wave
   static constexpr int kNQ = kWaveN / 32;                // 32x32 MFMA tiles along N per wave
@@ -369,7 +368,7 @@ struct Pipe {
   static constexpr int kChunkStages = DW ? 1 : 512 / kTK;  // stages per scale chunk
   static constexpr int kScaleRowBytes = DW ? 4 : 16;     // scale bytes per row per chunk
   static constexpr int kScaleBytes = 2 * 256 * kScaleRowBytes;  // A and B^T rows of a chunk
-  static constexpr int kAB = Stage<AE, kTK>::kBytes + Stage<BE, kTK, 4, TN>::kBytes;
+  static constexpr int kAB = Stage<AE, kTK, 4, TM>::kBytes + Stage<BE, kTK, 4, TN>::kBytes;
   static constexpr int kBuf = kAB + (DW ? kScaleBytes : 0);    // one stage buffer
   // As many stage buffers (4 or 2) as fit in 160 KiB (with two scale chunks).
   static constexpr int kStages = 4 * kBuf + (DW ? 0 : 2 * kScaleBytes) <= 160 * 1024 ? 4 : 2;
@@ -377,7 +376,7 @@ struct Pipe {
   static constexpr int kUnroll = 2 * kChunkStages > kStages ? 2 * kChunkStages : kStages;
   static_assert(kUnroll % kStages == 0, "buffer slots must repeat within the unrolled body");
   static constexpr int kDma =
-      Stage<AE, kTK, kWaves>::kInstr + Stage<BE, kTK, kWaves, TN>::kInstr;
+      Stage<AE, kTK, kWaves, TM>::kInstr + Stage<BE, kTK, kWaves, TN>::kInstr;
   // Scale chunk: 512 rows (A then B^T), 64 rows per load.
   static constexpr int kScaleDma = 8 / kWaves;           // per wave and chunk
   // Loads a wave issues along with stage s: its code tiles, plus the scale
@@ -397,15 +396,15 @@ __device__ __forceinline__ void unroll_seq(F&& f, std::integer_sequence<int, U..
   (f(std::integral_constant<int, U>{}), ...);
 }
 
-template <int AE, int BE, int TK, int WN, bool DW, int TN>
-__global__ void __launch_bounds__(128 * WN)
+template <int AE, int BE, int TK, int WN, bool DW, int TM, int TN>
+__global__ void __launch_bounds__(TM / 2 * WN)
 block_matmul_tiled(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa,
                    const uint8_t* __restrict__ b, const uint8_t* __restrict__ sb,
                    float* __restrict__ c, int64_t M, int64_t N, int64_t K, int64_t ldc,
                    int accumulate, int tiles_m, int tiles_n) {
-  using P = Pipe<AE, BE, TK, WN, DW, TN>;
+  using P = Pipe<AE, BE, TK, WN, DW, TM, TN>;
   constexpr int kTK = P::kTK, kChunkStages = P::kChunkStages, kWaves = P::kWaves;
-  constexpr int kA = Stage<AE, kTK>::kBytes, kAB = P::kAB, kStages = P::kStages;
+  constexpr int kA = Stage<AE, kTK, 4, TM>::kBytes, kAB = P::kAB, kStages = P::kStages;
   constexpr int kNQ = P::kNQ, kBuf = P::kBuf;
   constexpr int kScaleRowBytes = P::kScaleRowBytes, kScaleBytes = P::kScaleBytes;
   // One array per buffer, always indexed by a compile-time slot, so that the
@@ -431,7 +430,7 @@ block_matmul_tiled(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa
   const int gsize = min(tiles_m - first_m, kGroup);
   const int tm = first_m + (pid % in_group) % gsize;
   const int tn = (pid % in_group) / gsize;
-  const int64_t m0 = (int64_t)tm * kTM, n0 = (int64_t)tn * TN;
+  const int64_t m0 = (int64_t)tm * TM, n0 = (int64_t)tn * TN;
 
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -439,10 +438,10 @@ block_matmul_tiled(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa
   const uint32_t Ku = (uint32_t)K;
   const uint32_t a_row_bytes = AE == kE2M1 ? Ku / 2 : Ku;
   const uint32_t b_row_bytes = BE == kE2M1 ? Ku / 2 : Ku;
-  const Stager<AE, kTK, kWaves> stage_a(a_row_bytes, lane);
+  const Stager<AE, kTK, kWaves, TM> stage_a(a_row_bytes, lane);
   const Stager<BE, kTK, kWaves, TN> stage_b(b_row_bytes, lane);
   const uint32_t kblocks = Ku / 32;
-  const int64_t rows_a = min(M - m0, (int64_t)kTM), rows_b = min(N - n0, (int64_t)TN);
+  const int64_t rows_a = min(M - m0, (int64_t)TM), rows_b = min(N - n0, (int64_t)TN);
   // (a 256-row slab of either operand is below 2^31 bytes: checked at launch)
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(a + m0 * a_row_bytes, rows_a * a_row_bytes);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(b + n0 * b_row_bytes, rows_b * b_row_bytes);
@@ -588,19 +587,22 @@ block_matmul_tiled(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa
 
 // Launch configuration: 128-element K stages, 8 waves (2 x 4, 128 x 64 of C
 // each).  Two waves per SIMD let one wave's MFMAs run while the other waits
-// on LDS reads, its loads or the barrier.  The 256 x 128 tiles use 4 waves
-// (2 x 2) of the same 128 x 64 shape: 8 waves of 128 x 32 spill registers.
-constexpr int kTiledTK = 128, kTiledWN = 4, kHalfWN = 2;
+// on LDS reads, its loads or the barrier.  The 128 x 256 tiles of a last
+// round use 4 waves (1 x 4) of the same 128 x 64 shape; their stage (half
+// of A's rows) is small enough for four stage buffers where a whole tile's
+// E4M3 x E2M1 stage fits two.
+constexpr int kTiledTK = 128, kTiledWN = 4;
+constexpr int kTailTM = 128, kTailTN = 256, kTailWN = 4;
 
-template <int AE, int BE, bool DW, int TN, int WN>
+template <int AE, int BE, bool DW, int TM, int TN, int WN>
 hipError_t launch_tiled(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
                         float* c, int64_t M, int64_t N, int64_t K, int64_t ldc, int accumulate,
                         hipStream_t stream) {
   constexpr int TK = kTiledTK;
-  const int64_t tiles_m = (M + kTM - 1) / kTM, tiles_n = (N + TN - 1) / TN;
-  hipLaunchKernelGGL((block_matmul_tiled<AE, BE, TK, WN, DW, TN>),
+  const int64_t tiles_m = (M + TM - 1) / TM, tiles_n = (N + TN - 1) / TN;
+  hipLaunchKernelGGL((block_matmul_tiled<AE, BE, TK, WN, DW, TM, TN>),
                      dim3((unsigned)(tiles_m * tiles_n)),
-                     dim3(Pipe<AE, BE, TK, WN, DW, TN>::kThreads), 0, stream, a, sa, b, sb, c, M,
+                     dim3(Pipe<AE, BE, TK, WN, DW, TM, TN>::kThreads), 0, stream, a, sa, b, sb, c, M,
                      N, K, ldc, accumulate, (int)tiles_m, (int)tiles_n);
   return hipGetLastError();
 }
@@ -623,27 +625,31 @@ int cu_count() {
 // One workgroup per compute unit at a time, so 256x256 tiles run in rounds
 // of one tile per CU.  When the last round is at most half full (the
 // 2048 x 28672 prefill product: 896 tiles = 3.5 rounds of 256 CUs), the tile
-// columns holding it are computed by a second launch of 256x128 tiles, which
+// columns holding it are computed by a second launch of 128x256 tiles, which
 // fills the CUs in one round of half-size tiles; the rest of C is one launch
-// of whole rounds.  The two launches write disjoint columns of C.
+// of whole rounds.  The two launches write disjoint columns of C, and every
+// output element sums the same MFMAs in the same K order as in one launch.
 template <int AE, int BE, bool DW>
 hipError_t launch_tiled_split(const uint8_t* a, const uint8_t* sa, const uint8_t* b,
                               const uint8_t* sb, float* c, int64_t M, int64_t N, int64_t K,
                               int accumulate, hipStream_t stream) {
-  const int64_t tiles_m = (M + kTM - 1) / kTM, tiles_n = (N + 255) / 256;
+  const int64_t tiles_m = (M + 255) / 256, tiles_n = (N + 255) / 256;
   const int64_t tiles = tiles_m * tiles_n, cus = cu_count();
   const int64_t rem = tiles % cus;
   const int64_t tail_cols = (rem + tiles_m - 1) / tiles_m;  // tile columns of the last round
-  if (tiles > cus && rem != 0 && tail_cols < tiles_n && 2 * tiles_m * tail_cols <= cus) {
+  const int64_t tail_wgs = (M + kTailTM - 1) / kTailTM * (tail_cols * 256 / kTailTN);
+  if (tiles > cus && rem != 0 && tail_cols < tiles_n && tail_wgs <= cus) {
     const int64_t n1 = (tiles_n - tail_cols) * 256;
     const int64_t b_row_bytes = BE == kE2M1 ? K / 2 : K;
-    const hipError_t e =
-        launch_tiled<AE, BE, DW, 256, kTiledWN>(a, sa, b, sb, c, M, n1, K, N, accumulate, stream);
+    const hipError_t e = launch_tiled<AE, BE, DW, 256, 256, kTiledWN>(a, sa, b, sb, c, M, n1, K,
+                                                                      N, accumulate, stream);
     if (e != hipSuccess) return e;
-    return launch_tiled<AE, BE, DW, 128, kHalfWN>(a, sa, b + n1 * b_row_bytes, sb + n1 * (K / 32),
-                                         c + n1, M, N - n1, K, N, accumulate, stream);
+    return launch_tiled<AE, BE, DW, kTailTM, kTailTN, kTailWN>(
+        a, sa, b + n1 * b_row_bytes, sb + n1 * (K / 32), c + n1, M, N - n1, K, N, accumulate,
+        stream);
   }
-  return launch_tiled<AE, BE, DW, 256, kTiledWN>(a, sa, b, sb, c, M, N, K, N, accumulate, stream);
+  return launch_tiled<AE, BE, DW, 256, 256, kTiledWN>(a, sa, b, sb, c, M, N, K, N, accumulate,
+                                                      stream);
 }
 
 template <int AE, int BE>

@@ -216,8 +216,9 @@ def test_scale_array_alignment(offset):
 def test_tail_round_split(K, ae, accumulate):
     """M = 300, N = 33230: 2 x 130 = 260 tiles of 256 x 256 on 256 CUs leave
     a last round of 4 tiles, so the last 2 tile columns (N from 32768 on,
-    ragged at 462) are computed by a second launch of 256 x 128 tiles.  Both
-    scale-staging modes, with and without accumulation, every output."""
+    ragged at 462) are computed by a second launch of 128 x 256 tiles (M
+    ragged at 44 in the third).  Both scale-staging modes, with and without
+    accumulation, every output."""
     rng = np.random.default_rng(95 + K)
     M, N = 300, 33230
     ac, asc = quantized_normal(rng, M, K, ae)
