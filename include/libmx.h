@@ -32,12 +32,14 @@
  * `stream` (NULL = the default stream) and runs asynchronously: synchronize the
  * stream before reading results on the host.  Functions are thread-safe.
  *
- * Errors: arguments are validated before anything is enqueued; on any error
- * nothing is launched and nothing is written.  Validation is structural only
- * (null pointers, sizes, divisibility, element type, block size, alignment);
- * data never causes an error: a 0xFF scale decodes to NaN and a block of x
- * holding NaN or Inf quantizes to scale 0xFF with zero codes.  A failed
- * kernel launch returns MX_ERR_HIP.  Inputs and outputs must not overlap.
+ * Errors: arguments are validated before anything is enqueued; on a
+ * validation error nothing is launched and nothing is written.  Validation is
+ * structural only (null pointers, sizes, divisibility, element type, block
+ * size, alignment); data never causes an error: a 0xFF scale decodes to NaN
+ * and a block of x holding NaN or Inf quantizes to scale 0xFF with zero
+ * codes.  A failed kernel launch returns MX_ERR_HIP, and the outputs are then
+ * undefined (one call may enqueue more than one kernel).  Inputs and outputs
+ * must not overlap.
  */
 #ifndef LIBMX_H
 #define LIBMX_H
