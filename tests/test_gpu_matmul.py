@@ -212,25 +212,28 @@ def test_scale_array_alignment(offset):
     assert_matmul_close(got, want, mag)
 
 
-@pytest.mark.parametrize("K,ae,accumulate", [(512, O.E2M1, False), (640, O.E4M3, True)])
-def test_tail_round_split(K, ae, accumulate):
+@pytest.mark.parametrize("K,ae,be,accumulate", [(512, O.E2M1, O.E2M1, False),
+                                                (640, O.E4M3, O.E2M1, True),
+                                                (512, O.E4M3, O.E4M3, True),
+                                                (1024, O.E2M1, O.E4M3, False)])
+def test_tail_round_split(K, ae, be, accumulate):
     """M = 300, N = 33230: 2 x 130 = 260 tiles of 256 x 256 on 256 CUs leave
     a last round of 4 tiles, so the last 2 tile columns (N from 32768 on,
     ragged at 462) are computed by a second launch of 128 x 256 tiles (M
-    ragged at 44 in the third).  Both scale-staging modes, with and without
-    accumulation, every output."""
-    rng = np.random.default_rng(95 + K)
+    ragged at 44 in the third).  Every format pair, both scale-staging modes,
+    with and without accumulation, every output."""
+    rng = np.random.default_rng(95 + K + ae + 3 * be)
     M, N = 300, 33230
     ac, asc = quantized_normal(rng, M, K, ae)
-    bc, bsc = quantized_normal(rng, N, K, O.E2M1, sigma=0.02)
+    bc, bsc = quantized_normal(rng, N, K, be, sigma=0.02)
     cin = (rng.standard_normal((M, N)) * 10).astype(np.float32) if accumulate else None
-    got = gpu_matmul(ac, asc, ae, bc, bsc, O.E2M1, M, N, K, c_in=cin, accumulate=accumulate)
-    want, mag = O.block_matmul(ac, asc, ae, bc, bsc, O.E2M1, M, N, K, c_in=cin,
+    got = gpu_matmul(ac, asc, ae, bc, bsc, be, M, N, K, c_in=cin, accumulate=accumulate)
+    want, mag = O.block_matmul(ac, asc, ae, bc, bsc, be, M, N, K, c_in=cin,
                                accumulate=accumulate)
-    if ae == O.E2M1:
+    if ae == be == O.E2M1:
         assert_matmul_close(got, want, mag)
     else:
-        assert_t2(got, want, mag, ac, asc, ae, bc, bsc, O.E2M1, K)
+        assert_t2(got, want, mag, ac, asc, ae, bc, bsc, be, K)
 
 
 def test_mlp_down_projection_k11008():
