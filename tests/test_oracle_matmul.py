@@ -11,6 +11,8 @@ import pytest
 
 from oracle import mx_oracle as O
 
+from exact_rational import round_f32, value_exact
+
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
@@ -27,14 +29,7 @@ def _rand_operand(rng, rows, K, elem, byte_lo=118, byte_hi=136):
 
 
 def _value_exact(code, byte, elem):
-    if elem == O.E2M1:
-        s, e, m = code >> 3, (code >> 1) & 3, code & 1
-        mag = Fraction(2) ** (e - 1) * (1 + Fraction(m, 2)) if e else Fraction(m, 2)
-    else:
-        s, e, m = code >> 7, (code >> 3) & 15, code & 7
-        mag = Fraction(m, 8) * Fraction(2) ** -6 if e == 0 else Fraction(2) ** (e - 7) * (1 + Fraction(m, 8))
-    v = mag * Fraction(2) ** (int(byte) - 127)
-    return -v if s else v
+    return value_exact(code, byte, elem == O.E2M1)
 
 
 @pytest.mark.parametrize("a_elem,b_elem", [(O.E2M1, O.E2M1), (O.E4M3, O.E4M3), (O.E4M3, O.E2M1)])
@@ -49,8 +44,8 @@ def test_brute_force_exact_rationals(a_elem, b_elem, K):
         for n in range(N):
             exact = sum(_value_exact(int(ae[m, k]), asc[m, k // 32], a_elem) *
                         _value_exact(int(be[n, k]), bsc[n, k // 32], b_elem) for k in range(K))
-            # the exact sum rounded once to float32 (Python float is exact here)
-            assert c[m, n] == np.float32(float(exact))
+            # the exact sum rounded once to float32
+            assert c[m, n] == round_f32(exact)
             absum = sum(abs(_value_exact(int(ae[m, k]), asc[m, k // 32], a_elem) *
                             _value_exact(int(be[n, k]), bsc[n, k // 32], b_elem)) for k in range(K))
             # the tolerance scale only needs to be accurate, not exact
@@ -97,17 +92,53 @@ def test_scale_linearity():
         assert np.array_equal(c1, (c0.astype(np.float64) * 2.0 ** j).astype(np.float32))
 
 
-def test_accumulate_adds_c_in():
-    rng = np.random.default_rng(4)
-    M, N, K = 3, 3, 64
-    _, ac, asc = _rand_operand(rng, M, K, O.E2M1)
-    _, bc, bsc = _rand_operand(rng, N, K, O.E2M1)
-    c0, m0 = O.block_matmul(ac, asc, O.E2M1, bc, bsc, O.E2M1, M, N, K)
-    cin = rng.standard_normal((M, N)).astype(np.float32)
-    c1, m1 = O.block_matmul(ac, asc, O.E2M1, bc, bsc, O.E2M1, M, N, K, c_in=cin, accumulate=True)
-    exact = c0.astype(np.float64) + cin.astype(np.float64)
-    assert np.allclose(c1, exact, rtol=1e-7, atol=0)
-    assert np.array_equal(m1, m0 + np.abs(cin.astype(np.float64)))
+@pytest.mark.parametrize("a_elem,b_elem", [(O.E2M1, O.E2M1), (O.E4M3, O.E2M1), (O.E4M3, O.E4M3)])
+def test_accumulate_brute_force_exact_rationals(a_elem, b_elem):
+    # "The accumulator operand": C = C_in + A.B.  The oracle forms C_in + A.B
+    # exactly (every partial sum fits float64 at these sizes and scales) and
+    # rounds it to float32 once.
+    rng = np.random.default_rng(40 + a_elem * 3 + b_elem)
+    M, N, K = 3, 4, 64
+    ae, ac, asc = _rand_operand(rng, M, K, a_elem, 124, 131)
+    be, bc, bsc = _rand_operand(rng, N, K, b_elem, 124, 131)
+    cin = (rng.standard_normal((M, N)) * 2.0 ** rng.integers(-3, 4, (M, N))).astype(np.float32)
+    c, mag = O.block_matmul(ac, asc, a_elem, bc, bsc, b_elem, M, N, K, c_in=cin, accumulate=True)
+    for m in range(M):
+        for n in range(N):
+            terms = [_value_exact(int(ae[m, k]), asc[m, k // 32], a_elem) *
+                     _value_exact(int(be[n, k]), bsc[n, k // 32], b_elem) for k in range(K)]
+            exact = Fraction(float(cin[m, n])) + sum(terms)
+            assert c[m, n] == round_f32(exact)
+            absum = abs(Fraction(float(cin[m, n]))) + sum(abs(t) for t in terms)
+            assert abs(mag[m, n] - float(absum)) <= 1e-12 * float(absum)
+
+
+def _two_block_row(codes01, bytes01):
+    """One E2M1 row of K = 64: element 0 of block j has code codes01[j], the
+    rest are zero; block j has scale byte bytes01[j]."""
+    el = np.zeros((1, 64), np.uint8)
+    el[0, 0], el[0, 32] = codes01
+    return O.pack_nibbles(el), np.array([bytes01], np.uint8)
+
+
+@pytest.mark.parametrize("sign", [1.0, -1.0])
+def test_accumulate_rounds_once(sign):
+    # A.B = 2^-24 + 2^-50 (two blocks, 1.0 x 1.0 under scale bytes 115 and
+    # 102 on both sides) and C_in = 1: the exact sum 1 + 2^-24 + 2^-50 lies
+    # above the midpoint between 1 and 1 + 2^-23, so it rounds to 1 + 2^-23.
+    # Rounding A.B to float32 first (to 2^-24) and then adding C_in lands on
+    # the midpoint and rounds to even, 1.0: a double rounding fails here.
+    s = 0x8 if sign < 0 else 0x0
+    ac, asc = _two_block_row((0x2 | s, 0x2 | s), (115, 102))
+    bc, bsc = _two_block_row((0x2, 0x2), (115, 102))
+    cin = np.array([[sign]], np.float32)
+    c, _ = O.block_matmul(ac, asc, O.E2M1, bc, bsc, O.E2M1, 1, 1, 64, c_in=cin, accumulate=True)
+    exact = Fraction(int(sign)) * (1 + Fraction(1, 2 ** 24) + Fraction(1, 2 ** 50))
+    want = round_f32(exact)
+    assert want == np.float32(sign * (1 + 2.0 ** -23))
+    assert c[0, 0] == want
+    ab_first = np.float32(sign * (2.0 ** -24 + 2.0 ** -50))           # A.B rounded on its own
+    assert np.float32(np.float32(sign) + ab_first) != want          # the slip this pin catches
 
 
 def test_nan_scale_propagates_to_row_and_column():

@@ -19,6 +19,8 @@ import pytest
 
 from oracle import mx_oracle as O
 
+from exact_rational import round_f32, value_exact
+
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
@@ -163,16 +165,7 @@ def test_axis0_rejects_ragged_rows():
 
 # ----------------------------------------------------------- f32-B matmul
 def _exact_value(code, byte, elem):
-    if byte == 0xFF:
-        return None
-    if elem == O.E2M1:
-        s, e, m = code >> 3, (code >> 1) & 3, code & 1
-        mag = Fraction(2) ** (e - 1) * (1 + Fraction(m, 2)) if e else Fraction(m, 2)
-    else:
-        s, e, m = code >> 7, (code >> 3) & 15, code & 7
-        mag = Fraction(m, 8) * Fraction(2) ** -6 if e == 0 else Fraction(2) ** (e - 7) * (1 + Fraction(m, 8))
-    v = mag * Fraction(2) ** (int(byte) - 127)
-    return -v if s else v
+    return value_exact(code, byte, elem == O.E2M1)
 
 
 @pytest.mark.parametrize("elem", [O.E2M1, O.E4M3])
@@ -187,7 +180,7 @@ def test_f32b_brute_force_exact_rationals(elem, K):
         for n in range(N):
             terms = [_exact_value(int(el[m, k]), asc[m, k // 32], elem) * Fraction(float(b[k, n]))
                      for k in range(K)]
-            assert c[m, n] == np.float32(float(sum(terms)))
+            assert c[m, n] == round_f32(sum(terms))
             absum = float(sum(abs(t) for t in terms))
             assert abs(mag[m, n] - absum) <= 1e-12 * absum
 
@@ -212,16 +205,46 @@ def test_f32b_agrees_with_quantized_b_product():
     assert np.allclose(m1, m2, rtol=1e-15, atol=0)
 
 
-def test_f32b_accumulate_and_nan():
+def test_f32b_accumulate_brute_force_exact_rationals():
+    # "The accumulator operand" with the page's f32 B: C_in + A.B formed
+    # exactly and rounded to float32 once.
     rng = np.random.default_rng(23)
+    M, N, K = 4, 3, 64
+    el, ac, asc = _rand_operand(rng, M, K, O.E2M1)
+    b = (rng.standard_normal((K, N)) * np.exp2(rng.integers(-6, 6, (K, N)))).astype(np.float32)
+    cin = rng.standard_normal((M, N)).astype(np.float32)
+    c, mag = O.block_matmul_f32b(ac, asc, O.E2M1, b, M, N, K, c_in=cin, accumulate=True)
+    for m in range(M):
+        for n in range(N):
+            terms = [_exact_value(int(el[m, k]), asc[m, k // 32], O.E2M1) * Fraction(float(b[k, n]))
+                     for k in range(K)]
+            exact = Fraction(float(cin[m, n])) + sum(terms)
+            assert c[m, n] == round_f32(exact)
+            absum = float(abs(Fraction(float(cin[m, n]))) + sum(abs(t) for t in terms))
+            assert abs(mag[m, n] - absum) <= 1e-12 * absum
+
+
+def test_f32b_accumulate_rounds_once():
+    # A row: 1.0 and 0.5 under scale byte 103 (2^-24 and 2^-25); B column:
+    # 1.0 and 2^-25.  A.B = 2^-24 + 2^-50, C_in = 1: one rounding gives
+    # 1 + 2^-23, rounding A.B to float32 first gives 1.0.
+    el = np.zeros((1, 32), np.uint8)
+    el[0, 0], el[0, 1] = 0x2, 0x1
+    ac, asc = O.pack_nibbles(el), np.array([[103]], np.uint8)
+    b = np.zeros((32, 1), np.float32)
+    b[0, 0], b[1, 0] = 1.0, 2.0 ** -25
+    c, _ = O.block_matmul_f32b(ac, asc, O.E2M1, b, 1, 1, 32, c_in=np.ones((1, 1), np.float32),
+                               accumulate=True)
+    want = round_f32(1 + Fraction(1, 2 ** 24) + Fraction(1, 2 ** 50))
+    assert want == np.float32(1 + 2.0 ** -23) and c[0, 0] == want
+    assert np.float32(1.0) + np.float32(2.0 ** -24 + 2.0 ** -50) != want
+
+
+def test_f32b_nan_scale_poisons_its_row():
+    rng = np.random.default_rng(24)
     M, N, K = 4, 3, 64
     _, ac, asc = _rand_operand(rng, M, K, O.E2M1)
     b = rng.standard_normal((K, N)).astype(np.float32)
-    c0, m0 = O.block_matmul_f32b(ac, asc, O.E2M1, b, M, N, K)
-    cin = rng.standard_normal((M, N)).astype(np.float32)
-    c1, m1 = O.block_matmul_f32b(ac, asc, O.E2M1, b, M, N, K, c_in=cin, accumulate=True)
-    assert np.allclose(c1, c0.astype(np.float64) + cin, rtol=1e-7, atol=0)
-    assert np.array_equal(m1, m0 + np.abs(cin.astype(np.float64)))
     asc = asc.copy()
     asc[2, 1] = 0xFF
     c2, _ = O.block_matmul_f32b(ac, asc, O.E2M1, b, M, N, K)

@@ -235,6 +235,32 @@ def test_nonfinite_blocks_reading():
         assert not u[0, :32].any() and not u[1, 32:].any() and not u[2, :32].any()
 
 
+@pytest.mark.parametrize("name", ["nonfinite_inf_block", "nonfinite_inf_e4m3_block"])
+def test_nonfinite_page_literal_result_recorded(name):
+    # The golden records the page's own result for a block holding +-Inf next
+    # to reading R2's.  The oracle gives R2's (checked by test_worked_examples);
+    # here the page-literal record is checked for what makes R2 a departure:
+    # it is a different block, and it decodes to finite signed zeros only.
+    case = _golden_cases()[name]
+    elem = O.E2M1 if case["elem"] == "E2M1" else O.E4M3
+    lit = case["page_literal"]
+    assert lit["scale_byte"] == 254 and case["scale_byte"] == 255
+    head = [f32_from_bits(int(b, 16)) for b in case["x_head_bits"]]
+    el = np.zeros((1, 32), np.uint8)
+    el[0, :len(lit["codes_head"])] = lit["codes_head"]
+    codes = O.pack_nibbles(el) if elem == O.E2M1 else el
+    y = O.dequantize(codes, np.array([[lit["scale_byte"]]], np.uint8), elem, 32)[0]
+    assert np.all(y == 0.0)
+    # the sign survives and nothing else does
+    assert np.signbit(y[:len(head)]).tolist() == [h < 0 for h in head]
+    # steps of the derivation, through the oracle's own nearest-index rule:
+    # the grid is the same, the infinity keeps the first index, and finite
+    # values scaled by 2^-127 are far below half the smallest grid step
+    grid = O._format(elem)[0]
+    scaled = np.abs(np.array(head, np.float64)) * 2.0 ** -127
+    assert O._nearest_index(scaled, grid).tolist() == [0] * len(head)
+
+
 def test_shape_rule_rejects_ragged_blocks():
     with pytest.raises(ValueError):
         O.quantize(np.zeros((2, 48), np.float32), O.E2M1)
