@@ -1,8 +1,8 @@
 """ctypes binding of libmx (argument marshalling only).
 
 Every computation runs in the HIP kernels behind the C ABI declared in
-``include/libmx.h``; this module only checks tensor dtypes/devices/contiguity,
-allocates outputs with ``torch.empty`` on the tensors' device and passes raw
+``include/libmx.h``; this module only checks tensor dtypes, sizes, devices and
+contiguity, allocates outputs with ``torch.empty`` on the tensors' device and passes raw
 pointers plus the current HIP stream.  There is no CPU path: if the shared
 library is missing or fails to load, every call raises.
 """
@@ -132,16 +132,48 @@ def _stream_ptr(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _require(t, dtype, name):
+def _require(t, dtype, name, numel=None, shape=None, device=None, on_gpu=True):
+    """Type, contiguity and size of one tensor argument; then its device.
+
+    Every kernel trusts the sizes it is given, so a buffer shorter than the
+    shape passed to the ABI would be read or written out of bounds: sizes
+    are checked here, before any pointer reaches the library."""
     import torch
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if t.device.type != "cuda":
-        raise ValueError(f"{name} must live on a GPU device, got {t.device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} elements, got {t.numel()}")
+    if not on_gpu:
+        return
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on a GPU device, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the other operands on {device}")
+
+
+def _require_mx(t: "MXTensor", name: str, device=None, on_gpu=True):
+    """An MXTensor whose codes and scales hold exactly the bytes its rows,
+    cols, element type and block axis describe, on one device."""
+    if t.elem not in ELEM_NAMES:
+        raise ValueError(f"{name}: unsupported element type {t.elem}")
+    if t.axis not in (0, 1):
+        raise ValueError(f"{name}: block axis must be 0 or 1, got {t.axis}")
+    if t.rows < 0 or t.cols < 0:
+        raise ValueError(f"{name}: negative shape [{t.rows}, {t.cols}]")
+    import torch
+    sr, sc = (t.rows, t.cols) if t.axis == 1 else (t.cols, t.rows)
+    codes = sr * sc // 2 if t.elem == MX_E2M1 else sr * sc
+    _require(t.codes, torch.uint8, f"{name}.codes", numel=codes, on_gpu=False)
+    _require(t.scales, torch.uint8, f"{name}.scales", numel=sr * (sc // BLOCK), on_gpu=False)
+    if on_gpu:
+        _require(t.codes, torch.uint8, f"{name}.codes", device=device)
+        _require(t.scales, torch.uint8, f"{name}.scales", device=t.codes.device)
 
 
 @dataclass
@@ -182,16 +214,15 @@ def quantize(x, elem: int = MX_E2M1, out: MXTensor | None = None, axis: int = 1)
     """float32 [rows, cols] GPU tensor -> MXTensor blocked along `axis`
     (mx_quantize, or mx_quantize_axis for axis 0)."""
     import torch
-    _require(x, torch.float32, "x")
-    if x.dim() != 2:
-        raise ValueError("x must be 2-D [rows, cols]")
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("x must be a 2-D [rows, cols] tensor")
     rows, cols = x.shape
     if out is None:
         out = empty_mx(rows, cols, elem, x.device, axis)
     if (out.rows, out.cols, out.elem, out.axis) != (rows, cols, elem, axis):
         raise ValueError("out does not describe x's shape, element type and block axis")
-    _require(out.codes, torch.uint8, "codes")
-    _require(out.scales, torch.uint8, "scales")
+    _require_mx(out, "out")
+    _require(x, torch.float32, "x", device=out.codes.device)
     mx_quantize_axis(x.data_ptr(), out.codes.data_ptr(), out.scales.data_ptr(), rows, cols,
                      axis, elem, BLOCK, _stream_ptr(x.device))
     return out
@@ -200,11 +231,13 @@ def quantize(x, elem: int = MX_E2M1, out: MXTensor | None = None, axis: int = 1)
 def dequantize(t: MXTensor, out=None):
     """MXTensor -> float32 [rows, cols] GPU tensor (mx_dequantize_axis)."""
     import torch
-    _require(t.codes, torch.uint8, "codes")
-    _require(t.scales, torch.uint8, "scales")
+    _require_mx(t, "t", on_gpu=False)
+    if out is not None:
+        _require(out, torch.float32, "out", shape=(t.rows, t.cols), on_gpu=False)
+    _require_mx(t, "t")
     if out is None:
         out = torch.empty((t.rows, t.cols), dtype=torch.float32, device=t.codes.device)
-    _require(out, torch.float32, "out")
+    _require(out, torch.float32, "out", shape=(t.rows, t.cols), device=t.codes.device)
     mx_dequantize_axis(t.codes.data_ptr(), t.scales.data_ptr(), out.data_ptr(), t.rows, t.cols,
                        t.axis, t.elem, BLOCK, _stream_ptr(out.device))
     return out
@@ -212,8 +245,7 @@ def dequantize(t: MXTensor, out=None):
 
 def fold_scale(t: MXTensor, j: int) -> MXTensor:
     """In place: t becomes 2^j * t through its scale bytes (mx_fold_scale)."""
-    import torch
-    _require(t.scales, torch.uint8, "scales")
+    _require_mx(t, "t")
     mx_fold_scale(t.scales.data_ptr(), t.scales.numel(), j, _stream_ptr(t.scales.device))
     return t
 
@@ -229,14 +261,17 @@ def block_matmul(a: MXTensor, bt: MXTensor, out=None, accumulate: bool = False):
     if a.cols != bk:
         raise ValueError(f"K mismatch: A has {a.cols}, B has {bk}")
     M, N, K = a.rows, bn, a.cols
+    _require_mx(a, "a", on_gpu=False)
+    _require_mx(bt, "bt", on_gpu=False)
+    if out is not None:
+        _require(out, torch.float32, "out", shape=(M, N), on_gpu=False)
+    _require_mx(a, "a")
+    _require_mx(bt, "bt", device=a.codes.device)
     if out is None:
         if accumulate:
             raise ValueError("accumulate=True needs an existing out tensor")
         out = torch.empty((M, N), dtype=torch.float32, device=a.codes.device)
-    _require(out, torch.float32, "out")
-    for t, n in ((a.codes, "a.codes"), (a.scales, "a.scales"), (bt.codes, "bt.codes"),
-                 (bt.scales, "bt.scales")):
-        _require(t, torch.uint8, n)
+    _require(out, torch.float32, "out", shape=(M, N), device=a.codes.device)
     mx_block_matmul(a.codes.data_ptr(), a.scales.data_ptr(), a.elem, bt.codes.data_ptr(),
                     bt.scales.data_ptr(), bt.elem, out.data_ptr(), M, N, K, BLOCK,
                     1 if accumulate else 0, _stream_ptr(out.device))
@@ -249,17 +284,19 @@ def block_matmul_f32b(a: MXTensor, b, out=None, accumulate: bool = False):
     import torch
     if a.axis != 1:
         raise ValueError("A must be blocked along its last axis (K)")
-    _require(b, torch.float32, "b")
-    if b.dim() != 2 or b.shape[0] != a.cols:
-        raise ValueError(f"B must be [K={a.cols}, N], got {tuple(b.shape)}")
+    if not isinstance(b, torch.Tensor) or b.dim() != 2 or b.shape[0] != a.cols:
+        raise ValueError(f"B must be a [K={a.cols}, N] tensor")
     M, K, N = a.rows, a.cols, b.shape[1]
+    _require_mx(a, "a", on_gpu=False)
+    if out is not None:
+        _require(out, torch.float32, "out", shape=(M, N), on_gpu=False)
+    _require_mx(a, "a")
+    _require(b, torch.float32, "b", shape=(K, N), device=a.codes.device)
     if out is None:
         if accumulate:
             raise ValueError("accumulate=True needs an existing out tensor")
         out = torch.empty((M, N), dtype=torch.float32, device=b.device)
-    _require(out, torch.float32, "out")
-    _require(a.codes, torch.uint8, "a.codes")
-    _require(a.scales, torch.uint8, "a.scales")
+    _require(out, torch.float32, "out", shape=(M, N), device=a.codes.device)
     mx_block_matmul_f32b(a.codes.data_ptr(), a.scales.data_ptr(), a.elem, b.data_ptr(),
                          out.data_ptr(), M, N, K, BLOCK, 1 if accumulate else 0,
                          _stream_ptr(out.device))

@@ -145,6 +145,47 @@ def test_python_layer_rejects_cpu_tensors(L):
         B.quantize(torch.zeros(4, 64))
 
 
+def _mx(rows, cols, elem, codes_n=None, scales_n=None, axis=1):
+    """An MXTensor of CPU buffers, with the right sizes unless overridden."""
+    import torch
+    sr, sc = (rows, cols) if axis == 1 else (cols, rows)
+    cn = sr * sc // 2 if elem == B.MX_E2M1 else sr * sc
+    codes = torch.zeros(cn if codes_n is None else codes_n, dtype=torch.uint8)
+    scales = torch.zeros(sr * sc // 32 if scales_n is None else scales_n, dtype=torch.uint8)
+    return B.MXTensor(codes, scales, rows, cols, elem, axis)
+
+
+def test_python_layer_checks_buffer_sizes(L):
+    """A buffer that does not match the shape handed to the ABI is refused
+    before any pointer reaches a kernel (a short one would be read or
+    written out of bounds)."""
+    import torch
+    size = "must hold|must have shape"
+    with pytest.raises(ValueError, match=size):                   # quantize into a short out
+        B.quantize(torch.zeros(4, 64), B.MX_E2M1, out=_mx(4, 64, B.MX_E2M1, codes_n=100))
+    with pytest.raises(ValueError, match=size):
+        B.quantize(torch.zeros(4, 64), B.MX_E4M3, out=_mx(4, 64, B.MX_E4M3, scales_n=7))
+    with pytest.raises(ValueError, match=size):                   # rows/cols that lie
+        B.dequantize(_mx(4, 64, B.MX_E2M1, codes_n=96))
+    with pytest.raises(ValueError, match=size):
+        B.dequantize(_mx(4, 64, B.MX_E2M1), out=torch.zeros(4, 32))
+    with pytest.raises(ValueError, match=size):                   # axis-0 storage
+        B.dequantize(_mx(64, 4, B.MX_E4M3, codes_n=64 * 3, axis=0))
+    with pytest.raises(ValueError, match=size):
+        B.fold_scale(_mx(4, 64, B.MX_E2M1, scales_n=9), 1)
+    a, bt = _mx(8, 64, B.MX_E4M3), _mx(16, 64, B.MX_E2M1)
+    with pytest.raises(ValueError, match=size):                   # C of the wrong shape
+        B.block_matmul(a, bt, out=torch.zeros(8, 15))
+    with pytest.raises(ValueError, match=size):
+        B.block_matmul(_mx(8, 64, B.MX_E4M3, codes_n=8 * 63), bt)
+    with pytest.raises(ValueError, match=size):
+        B.block_matmul(a, _mx(16, 64, B.MX_E2M1, scales_n=31))
+    with pytest.raises(ValueError, match=size):
+        B.block_matmul_f32b(a, torch.zeros(64, 5), out=torch.zeros(8, 6))
+    with pytest.raises(ValueError, match="element type"):
+        B.dequantize(B.MXTensor(torch.zeros(4), torch.zeros(4), 1, 32, 7))
+
+
 def test_build_rejects_kernels_that_spill():
     """The build parses the compiler's resource-usage remarks and names every
     kernel with scratch memory (the tiled matmul's hand-counted load waits
