@@ -100,6 +100,98 @@ def test_value_sweep_with_anchor(elem):
     assert np.all(scales == 127)
 
 
+def _bits(v):
+    return np.asarray(v, np.float32).view(np.uint32).astype(np.int64)
+
+
+def _f32(bits):
+    return np.asarray(bits, np.int64).astype(np.uint32).view(np.float32)
+
+
+def _blocks_of(anchor_bits, vals, shifts):
+    """Blocks [anchor, 31 values] for every power-of-two shift 2^j of the
+    whole block, padded (by repeating blocks) to a multiple of 32 blocks:
+    the kernel quantizes 32 blocks per wave and zero-fills a partial set,
+    and a zero element would send the wave down its exact path."""
+    nb = -(-vals.size // 31)
+    flat = np.resize(vals, nb * 31).astype(np.float32)
+    base = np.empty((nb, 32), np.float32)
+    base[:, 0] = _f32(anchor_bits)
+    base[:, 1:] = flat.reshape(nb, 31)
+    x = np.concatenate([base * np.float32(2.0 ** j) for j in shifts])
+    pad = (-x.shape[0]) % 32
+    return np.concatenate([x, x[:pad]]) if pad else x
+
+
+@pytest.mark.parametrize("elem", ELEMS)
+def test_hardware_convert_near_every_midpoint(elem):
+    """Values within 1..8 ulp of every rounding midpoint and grid value, both
+    signs, never exactly on one, with an anchor whose low mantissa bits are
+    not zero: every wave of this input rounds with gfx950's scaled convert
+    (the exact fallback only runs for waves holding a value whose low
+    mantissa bits are all zero, such as a midpoint, a grid value or 0).
+    The whole block is also shifted by 2^j over a wide range, which moves
+    the scale the convert applies while y stays the same."""
+    if elem == O.E2M1:
+        grid, anchor, low_bits = O.e2m1_magnitudes(), 0x40FFFFFF, 21    # 7.9999995, e = 0
+    else:
+        grid, anchor, low_bits = O.e4m3_magnitudes(), 0x43FFFFFF, 19    # 511.99997, e = 0
+    mids = (grid[:-1] + grid[1:]) / 2
+    pts = _bits(np.concatenate([mids, grid[1:], [448.0 + 16.0]] if elem == O.E4M3
+                               else [mids, grid[1:]]))
+    near = np.concatenate([pts + d for d in range(-8, 9) if d != 0])
+    vals = _f32(near)
+    vals = vals[(vals < _f32(anchor)) & (vals > 0)]
+    assert np.all((_bits(vals) & ((1 << low_bits) - 1)) != 0)
+    vals = np.concatenate([vals, -vals])
+    shifts = range(-100, 121 if elem == O.E2M1 else 118)   # the anchor stays finite
+    x = _blocks_of(anchor, vals, shifts)
+    assert np.all(np.isfinite(x)) and np.all((_bits(x) & ((1 << low_bits) - 1)) != 0)
+    codes, scales = check_quantize(x, elem, "near midpoints")
+    assert set(np.unique(scales).tolist()) == {127 + j for j in shifts}
+
+
+@pytest.mark.parametrize("elem", ELEMS)
+def test_subnormal_elements_in_a_normal_block(elem):
+    """f32 subnormals of both signs next to a normal block maximum: they all
+    round to zero magnitude, the negative ones keep their sign bit (code 0x8
+    or 0x80), on the hardware-convert path (no element has its low mantissa
+    bits all zero)."""
+    anchor = 0x40FFFFFF if elem == O.E2M1 else 0x43FFFFFF
+    sub = np.arange(1, 0x800000, 4099, dtype=np.int64)
+    sub = sub[(sub & 0x1FFFFF) != 0]
+    vals = np.concatenate([_f32(sub), -_f32(sub)])
+    x = _blocks_of(anchor, vals, [0])
+    codes, _ = check_quantize(x, elem, "subnormal elements")
+    el = O.unpack_nibbles(codes) if elem == O.E2M1 else codes
+    assert np.all((el[:, 1:] & (0x7 if elem == O.E2M1 else 0x7F)) == 0)
+
+
+def test_e2m1_exhaustive_sweep():
+    """Every float32 in [2^-3, 8), both signs (100,663,296 values), 31 per
+    block after an anchor forcing e = 0, against the oracle."""
+    lo, hi = 0x3E000000, 0x41000000
+    allv = np.arange(lo, hi, dtype=np.uint32).view(np.float32)
+    vals = np.concatenate([allv, -allv])
+    del allv
+    nb = -(-vals.size // 31)
+    flat = np.zeros(nb * 31, np.float32)
+    flat[:vals.size] = vals
+    del vals
+    x = np.empty((nb, 32), np.float32)
+    x[:, 0] = 7.0
+    x[:, 1:] = flat.reshape(nb, 31)
+    del flat
+    gc, gs = gpu_quantize(x, O.E2M1)
+    assert np.all(gs == 127)
+    step = 1 << 20
+    for r0 in range(0, nb, step):
+        oc, os_ = O.quantize(x[r0:r0 + step], O.E2M1)
+        assert_bits_equal(gs[r0:r0 + step], os_, f"scales, blocks {r0}..")
+        assert_bits_equal(gc[r0:r0 + step], oc, f"codes, blocks {r0}..")
+        print(f"exhaustive E2M1 sweep: blocks {r0}..{min(nb, r0 + step)} of {nb} match", flush=True)
+
+
 @pytest.mark.parametrize("elem", ELEMS)
 def test_exhaustive_decode(elem):
     if elem == O.E2M1:
@@ -141,29 +233,31 @@ def test_ragged_sizes_and_guard_bytes(elem, rows, cols):
 
 def test_weight_codec_full_size():
     """8192x8192 N(0, 0.02) with 0.1% outliers x50, quantized in one launch as
-    the benchmark does; bit-exact on sampled rows, dequantize bit-exact in full."""
+    the benchmark does: every code and scale, and every dequantized value,
+    bit-exact."""
     x = W.weight_codec_case()
     xd = dev(x)
     t = B.quantize(xd, O.E2M1)
     gc, gs = host(t.codes), host(t.scales)
-    rng = np.random.default_rng(42)
-    rows = np.unique(np.concatenate([[0, 8191], rng.choice(8192, 254, replace=False)]))
-    oc, os_ = O.quantize(x[rows], O.E2M1)
-    assert_bits_equal(gs[rows], os_, "scales (sampled rows)")
-    assert_bits_equal(gc[rows], oc, "codes (sampled rows)")
+    step = 1024
+    for r0 in range(0, 8192, step):
+        oc, os_ = O.quantize(x[r0:r0 + step], O.E2M1)
+        assert_bits_equal(gs[r0:r0 + step], os_, f"scales, rows {r0}..")
+        assert_bits_equal(gc[r0:r0 + step], oc, f"codes, rows {r0}..")
     y = host(B.dequantize(t))
     assert_bits_equal(y, O.dequantize(gc, gs, O.E2M1, 8192), "dequantize full")
 
 
 def test_prefill_activation_quantize_full_size():
-    """2048x8192 activations (0.5% outliers x20) to E4M3, sampled rows."""
+    """2048x8192 activations (0.5% outliers x20) to E4M3: every code and scale."""
     a, _ = W.prefill_linear_case(N=32)
     t = B.quantize(dev(a), O.E4M3)
     gc, gs = host(t.codes), host(t.scales)
-    rows = np.unique(np.concatenate([[0, 2047], np.random.default_rng(5).choice(2048, 30, replace=False)]))
-    oc, os_ = O.quantize(a[rows], O.E4M3)
-    assert_bits_equal(gs[rows], os_, "scales")
-    assert_bits_equal(gc[rows], oc, "codes")
+    step = 256
+    for r0 in range(0, 2048, step):
+        oc, os_ = O.quantize(a[r0:r0 + step], O.E4M3)
+        assert_bits_equal(gs[r0:r0 + step], os_, f"scales, rows {r0}..")
+        assert_bits_equal(gc[r0:r0 + step], oc, f"codes, rows {r0}..")
 
 
 @pytest.mark.parametrize("elem", ELEMS)
