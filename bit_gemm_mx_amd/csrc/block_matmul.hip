@@ -289,8 +289,9 @@ block_matmul_skinny(const uint8_t* __restrict__ a, const uint8_t* __restrict__ s
 
 // ---------------------------------------------------------------------------
 // Tiled kernel: TM x TN output tile (256 x 256, or 128 x 256 for a last
-// round of tiles) per workgroup of (TM / 128) x WN waves, each wave
-// 128 x (TN / WN) = 4 x (TN / 32 / WN) tiles of the 32x32x64 scaled MFMA.
+// round of tiles) per workgroup of WM x WN waves, each wave (TM / WM) x
+// (TN / WN) of C = (TM / WM / 32) x (TN / WN / 32) tiles of the 32x32x64
+// scaled MFMA.
 //
 // K runs in stages of TK elements (TK / 64 MFMA K steps).  Code tiles are
 // staged straight into LDS by buffer loads that write LDS, two or four stage
@@ -405,11 +406,14 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4)
 // Stage mode (K a multiple of 128, DW): one dword per row (the stage's 4
 // blocks) with every stage, stored after the stage's code tiles in the same
 // stage buffer.
-template <int AE, int BE, int TK, int WN, bool DW, int TM, int TN>
+template <int AE, int BE, int TK, int WM, int WN, bool DW, int TM, int TN>
 struct Pipe {
   static constexpr int kTK = TK;
-  static constexpr int kWaves = TM / 128 * WN;           // TM / 128 along M, WN along N
+  static constexpr int kWaves = WM * WN;                 // WM along M, WN along N
   static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kWaveM = TM / WM;                 // rows of C per wave
+  static constexpr int kMQ = kWaveM / 32;                // 32x32 MFMA tiles along M per wave
+  static_assert(kMQ >= 1 && kMQ * 32 * WM == TM, "whole 32-row MFMA tiles per wave");
   static constexpr int kWaveN = TN / WN;                 // columns of C per wave
   static constexpr int kNQ = kWaveN / 32;                // 32x32 MFMA tiles along N per wave
   static_assert(kNQ >= 1 && kNQ * 32 * WN == TN, "whole 32-column MFMA tiles per wave");
@@ -446,16 +450,16 @@ __device__ __forceinline__ void unroll_seq(F&& f, std::integer_sequence<int, U..
   (f(std::integral_constant<int, U>{}), ...);
 }
 
-template <int AE, int BE, int TK, int WN, bool DW, int TM, int TN>
-__global__ void __launch_bounds__(TM / 2 * WN)
+template <int AE, int BE, int TK, int WM, int WN, bool DW, int TM, int TN>
+__global__ void __launch_bounds__(64 * WM * WN)
 block_matmul_tiled(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa,
                    const uint8_t* __restrict__ b, const uint8_t* __restrict__ sb,
                    float* __restrict__ c, int64_t M, int64_t N, int64_t K, int64_t ldc,
                    int accumulate, int tiles_m, int tiles_n) {
-  using P = Pipe<AE, BE, TK, WN, DW, TM, TN>;
+  using P = Pipe<AE, BE, TK, WM, WN, DW, TM, TN>;
   constexpr int kTK = P::kTK, kChunkStages = P::kChunkStages, kWaves = P::kWaves;
   constexpr int kA = Stage<AE, kTK, 4, TM>::kBytes, kAB = P::kAB, kStages = P::kStages;
-  constexpr int kNQ = P::kNQ, kBuf = P::kBuf;
+  constexpr int kMQ = P::kMQ, kNQ = P::kNQ, kBuf = P::kBuf;
   constexpr int kScaleRowBytes = P::kScaleRowBytes, kScaleBytes = P::kScaleBytes;
   // One array per buffer, always indexed by a compile-time slot, so that the
   // compiler can tell the direct-to-LDS loads into one buffer from the reads
@@ -498,11 +502,11 @@ block_matmul_tiled(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa
   const __amdgpu_buffer_rsrc_t rsa = make_rsrc(sa + m0 * kblocks, rows_a * kblocks);
   const __amdgpu_buffer_rsrc_t rsb = make_rsrc(sb + n0 * kblocks, rows_b * kblocks);
   // This lane's first A / B^T tile row.
-  const int ar = wm * 128 + lr, br = wn * P::kWaveN + lr;
+  const int ar = wm * P::kWaveM + lr, br = wn * P::kWaveN + lr;
 
-  v16f acc[4][kNQ];
+  v16f acc[kMQ][kNQ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kMQ; ++i)
 #pragma unroll
     for (int j = 0; j < kNQ; ++j)
 #pragma unroll
@@ -557,7 +561,7 @@ block_matmul_tiled(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa
   // (Not for an E4M3 B: FP8 x FP8 measured faster with the dword reads, and
   // E2M1 x E4M3 needs the registers for its split B operand.)
   constexpr bool kScaleRegs = !DW && BE == kE2M1;
-  v4i sa4[4], sb4[kNQ];
+  v4i sa4[kMQ], sb4[kNQ];
   auto stage = [&](auto U) {
     constexpr int u = decltype(U)::value;
     constexpr int buf = u % kStages, par = u / kChunkStages % 2, sub = u % kChunkStages;
@@ -579,10 +583,10 @@ block_matmul_tiled(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa
     // scale dword holding them, shifted so that byte sel0 + 2h holds this
     // lane's block of K step h (lane group g takes block g of each step).
     constexpr int blk0 = sub * (kTK / 32), sel0 = blk0 % 4;
-    int sas[4], sbs[kNQ];
+    int sas[kMQ], sbs[kNQ];
     if constexpr (!kScaleRegs) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kMQ; ++i)
         sas[i] = (int)(*reinterpret_cast<const uint32_t*>(sc + (ar + 32 * i) * kScaleRowBytes +
                                                           (blk0 & ~3)) >> (8 * g));
 #pragma unroll
@@ -593,7 +597,7 @@ block_matmul_tiled(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa
     } else {
       if constexpr (sub == 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < kMQ; ++i)
           sa4[i] = *reinterpret_cast<const v4i*>(sc + (ar + 32 * i) * kScaleRowBytes);
 #pragma unroll
         for (int q = 0; q < kNQ; ++q)
@@ -601,22 +605,22 @@ block_matmul_tiled(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa
                                                  (br + 32 * q) * kScaleRowBytes);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sas[i] = (int)((uint32_t)sa4[i][blk0 / 4] >> (8 * g));
+      for (int i = 0; i < kMQ; ++i) sas[i] = (int)((uint32_t)sa4[i][blk0 / 4] >> (8 * g));
 #pragma unroll
       for (int q = 0; q < kNQ; ++q) sbs[q] = (int)((uint32_t)sb4[q][blk0 / 4] >> (8 * g));
     }
     auto kstep = [&](auto H) {
       constexpr int h = decltype(H)::value;
-      v8i af[4], bf[kNQ];
+      v8i af[kMQ], bf[kNQ];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = read_operand<AE, kTK>(la, ar + 32 * i, h, g);
+      for (int i = 0; i < kMQ; ++i) af[i] = read_operand<AE, kTK>(la, ar + 32 * i, h, g);
 #pragma unroll
       for (int q = 0; q < kNQ; ++q) bf[q] = read_operand<BE, kTK>(lb, br + 32 * q, h, g);
       constexpr int sel = sel0 + 2 * h;
       constexpr int fa = Operand<AE>::kFmt, fb = Operand<BE>::kFmt;
       if constexpr (Split<AE, BE>::kA) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < kMQ; ++i) {
           const v8i ah = e4m3_high(af[i]), al = af[i] ^ ah;
 #pragma unroll
           for (int q = 0; q < kNQ; ++q) {
@@ -631,7 +635,7 @@ block_matmul_tiled(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa
         for (int q = 0; q < kNQ; ++q) {
           const v8i bh = e4m3_high(bf[q]), bl = bf[q] ^ bh;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
+          for (int i = 0; i < kMQ; ++i) {
             acc[i][q] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                 af[i], bh, acc[i][q], fa, fb, sel, sas[i], sel, sbs[q]);
             acc[i][q] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
@@ -640,7 +644,7 @@ block_matmul_tiled(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < kMQ; ++i)
 #pragma unroll
           for (int q = 0; q < kNQ; ++q)
             acc[i][q] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
@@ -653,7 +657,7 @@ block_matmul_tiled(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa
     // first K step, then one MFMA, one global load and one LDS read at a
     // time, so that the loads of the next stage drain through the memory
     // pipeline while the MFMAs run instead of stalling the wave in a burst.
-    constexpr int kMfma = 4 * kNQ * P::kSteps * (Split<AE, BE>::kA || Split<AE, BE>::kB ? 2 : 1);
+    constexpr int kMfma = kMQ * kNQ * P::kSteps * (Split<AE, BE>::kA || Split<AE, BE>::kB ? 2 : 1);
     constexpr int kVmem = P::kDma + (nu % kChunkStages == 0 ? P::kScaleDma : 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);  // LDS reads
 #pragma unroll
@@ -673,13 +677,13 @@ block_matmul_tiled(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa
   // caches, would evict the operands that later tiles still read from the
   // Infinity Cache (measured 4% faster on the 8192^3 FP8 product).
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kMQ; ++i)
 #pragma unroll
     for (int q = 0; q < kNQ; ++q) {
       const int64_t col = n0 + wn * P::kWaveN + 32 * q + lr;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int64_t row = m0 + wm * 128 + 32 * i + 8 * (e >> 2) + 4 * g + (e & 3);
+        const int64_t row = m0 + wm * P::kWaveM + 32 * i + 8 * (e >> 2) + 4 * g + (e & 3);
         if (row < M && col < N) {
           float v = acc[i][q][e];
           if (accumulate) v += c[row * ldc + col];
@@ -689,25 +693,35 @@ block_matmul_tiled(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa
     }
 }
 
-// Launch configuration: 128-element K stages, 8 waves (2 x 4, 128 x 64 of C
-// each).  Two waves per SIMD let one wave's MFMAs run while the other waits
-// on LDS reads, its loads or the barrier.  The 128 x 256 tiles of a last
-// round use 4 waves (1 x 4) of the same 128 x 64 shape; their stage (half
-// of A's rows) is small enough for four stage buffers where a whole tile's
-// E4M3 x E2M1 stage fits two.
-constexpr int kTiledTK = 128, kTiledWN = 4;
-constexpr int kTailTM = 128, kTailTN = 256, kTailWN = 4;
+// Launch configuration: 128-element K stages, 8 waves.  Two waves per SIMD
+// let one wave's MFMAs run while the other waits on LDS reads, its loads or
+// the barrier.  Wave tiles are 128 x 64 of C (2 x 4 waves), or 64 x 128
+// (4 x 2) when A's E4M3 codes are split: each wave then splits two A tiles
+// per K step instead of four (the split is VALU work), and its LDS reads
+// (two 32-byte A operands and four 16-byte E2M1 ones per lane) are 20%
+// fewer.  The 128 x 256 tiles of a last round use 4 waves of the same wave
+// tile; their stage (half of A's rows) is small enough for four stage
+// buffers where a whole tile's E4M3 x E2M1 stage fits two.
+constexpr int kTiledTK = 128;
+constexpr int kTailTM = 128, kTailTN = 256;
 
-template <int AE, int BE, bool DW, int TM, int TN, int WN>
+template <int AE, int BE>
+struct WaveGrid {
+  static constexpr int kWM = Split<AE, BE>::kA ? 4 : 2;  // whole 256 x 256 tiles
+  static constexpr int kWN = 8 / kWM;
+  static constexpr int kTailWM = kWM / 2, kTailWN = kWN;  // 128 x 256 tiles
+};
+
+template <int AE, int BE, bool DW, int TM, int TN, int WM, int WN>
 hipError_t launch_tiled(const uint8_t* a, const uint8_t* sa, const uint8_t* b, const uint8_t* sb,
                         float* c, int64_t M, int64_t N, int64_t K, int64_t ldc, int accumulate,
                         hipStream_t stream) {
   constexpr int TK = kTiledTK;
   const int64_t tiles_m = (M + TM - 1) / TM, tiles_n = (N + TN - 1) / TN;
-  hipLaunchKernelGGL((block_matmul_tiled<AE, BE, TK, WN, DW, TM, TN>),
+  hipLaunchKernelGGL((block_matmul_tiled<AE, BE, TK, WM, WN, DW, TM, TN>),
                      dim3((unsigned)(tiles_m * tiles_n)),
-                     dim3(Pipe<AE, BE, TK, WN, DW, TM, TN>::kThreads), 0, stream, a, sa, b, sb, c, M,
-                     N, K, ldc, accumulate, (int)tiles_m, (int)tiles_n);
+                     dim3(Pipe<AE, BE, TK, WM, WN, DW, TM, TN>::kThreads), 0, stream, a, sa, b, sb,
+                     c, M, N, K, ldc, accumulate, (int)tiles_m, (int)tiles_n);
   return hipGetLastError();
 }
 
@@ -737,6 +751,7 @@ template <int AE, int BE, bool DW>
 hipError_t launch_tiled_split(const uint8_t* a, const uint8_t* sa, const uint8_t* b,
                               const uint8_t* sb, float* c, int64_t M, int64_t N, int64_t K,
                               int accumulate, hipStream_t stream) {
+  using G = WaveGrid<AE, BE>;
   const int64_t tiles_m = (M + 255) / 256, tiles_n = (N + 255) / 256;
   const int64_t tiles = tiles_m * tiles_n, cus = cu_count();
   const int64_t rem = tiles % cus;
@@ -745,15 +760,15 @@ hipError_t launch_tiled_split(const uint8_t* a, const uint8_t* sa, const uint8_t
   if (tiles > cus && rem != 0 && tail_cols < tiles_n && tail_wgs <= cus) {
     const int64_t n1 = (tiles_n - tail_cols) * 256;
     const int64_t b_row_bytes = BE == kE2M1 ? K / 2 : K;
-    const hipError_t e = launch_tiled<AE, BE, DW, 256, 256, kTiledWN>(a, sa, b, sb, c, M, n1, K,
-                                                                      N, accumulate, stream);
+    const hipError_t e = launch_tiled<AE, BE, DW, 256, 256, G::kWM, G::kWN>(
+        a, sa, b, sb, c, M, n1, K, N, accumulate, stream);
     if (e != hipSuccess) return e;
-    return launch_tiled<AE, BE, DW, kTailTM, kTailTN, kTailWN>(
+    return launch_tiled<AE, BE, DW, kTailTM, kTailTN, G::kTailWM, G::kTailWN>(
         a, sa, b + n1 * b_row_bytes, sb + n1 * (K / 32), c + n1, M, N - n1, K, N, accumulate,
         stream);
   }
-  return launch_tiled<AE, BE, DW, 256, 256, kTiledWN>(a, sa, b, sb, c, M, N, K, N, accumulate,
-                                                      stream);
+  return launch_tiled<AE, BE, DW, 256, 256, G::kWM, G::kWN>(a, sa, b, sb, c, M, N, K, N,
+                                                            accumulate, stream);
 }
 
 template <int AE, int BE>
