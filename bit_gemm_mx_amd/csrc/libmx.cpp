@@ -129,7 +129,7 @@ const char* mx_status_string(mx_status_t status) {
     case MX_ERR_NULL: return "a required pointer is NULL";
     case MX_ERR_SHAPE: return "invalid shape: sizes must be >= 1 and cols/K a multiple of 32";
     case MX_ERR_UNSUPPORTED: return "unsupported element type or block size (E2M1/E4M3, 32)";
-    case MX_ERR_ALIGN: return "buffer not 16-byte aligned";
+    case MX_ERR_ALIGN: return "buffer below the required alignment (16 bytes; 4 for the f32-B product's B and C)";
     case MX_ERR_HIP: return "HIP runtime error at kernel launch";
   }
   return "unknown status";
