@@ -20,8 +20,14 @@ matmul (HBM-bound), the MXFP8 8192^3 product, the prefill linear layer
 with blocks along axis 0 on the 8192x8192 weight workload, and fold_scale on
 its scales.  Kernel durations come from HIP events recorded on the stream the
 kernels run on (for the parts, around replays of a HIP graph of back-to-back
-calls).  The CPU oracle is timed on a bounded sample of the step's
-workload as `cpu_baseline`.
+calls).
+
+Before the GPU is touched, the CPU oracle runs on the host's cores (one
+worker process per available core, at most 16): whole passes of the step's
+workload give `cpu_baseline` and the bit-exact reference of the step's
+outputs (`parity`); the oracle's float64 block_matmul is timed on each matmul
+workload (in full for the decode shape, on stated output samples for the
+others) and its outputs are the reference of each matmul part's `parity`.
 """
 
 from __future__ import annotations
@@ -55,6 +61,25 @@ def codec_bytes(rows: int, cols: int, elem_bytes: float) -> int:
 def matmul_bytes(M, N, K, a_bytes, b_bytes, accumulate=False) -> int:
     return int(M * K * a_bytes + M * K // 32 + N * K * b_bytes + N * K // 32 +
                M * N * 4 * (2 if accumulate else 1))
+
+
+FLOOR_SRC = os.path.join(ROOT, "bench_floor.hip")
+FLOOR_LIB = os.path.join(ROOT, "bench_floor.so")
+
+
+def build_floor() -> str:
+    """Compile bench_floor.hip (the decode product's memory-floor reference)
+    into bench_floor.so beside this file."""
+    import subprocess
+    from bit_gemm_mx_amd.build import ARCH, hipcc
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", FLOOR_SRC,
+           "-o", FLOOR_LIB + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on bench_floor.hip:\n{r.stderr}")
+    os.replace(FLOOR_LIB + ".tmp", FLOOR_LIB)
+    return FLOOR_LIB
 
 
 def source_hash(*names: str) -> str:
@@ -100,7 +125,7 @@ class EventTimer:
         return float(np.mean(v)), float(np.min(v))
 
 
-def bench_codec(mx, W, torch, steps, warmup):
+def bench_codec(mx, W, torch, steps, warmup, ref=None):
     rows = cols = 8192
     x_host = W.weight_codec_case(rows, cols, seed=1002)
     copies = 4
@@ -151,9 +176,22 @@ def bench_codec(mx, W, torch, steps, warmup):
         "dequantize_e2m1": dict(ms=d_ms, min_ms=d_min, bytes=per_op, src="dequantize.hip",
                                 kernel="dequantize_kernel<1>"),
     }
+    parity = None
+    if ref is not None:
+        # every copy holds the same workload: check copy 0's step outputs
+        oc, os_, oy = ref
+        same = lambda g, w: bool(np.array_equal(g.view(np.uint8) if g.dtype != np.float32
+                                                else g.view(np.uint32),
+                                                w.view(np.uint8) if w.dtype != np.float32
+                                                else w.view(np.uint32)))
+        parity = {"elements": rows * cols,
+                  "codes_bit_exact": same(qs[0].codes.cpu().numpy(), oc),
+                  "scales_bit_exact": same(qs[0].scales.cpu().numpy(), os_),
+                  "dequantized_bit_exact": same(ys[0].cpu().numpy(), oy),
+                  "against": "the oracle's quantize and dequantize of the same input"}
     del xs, qs, ys
     torch.cuda.empty_cache()
-    return wall, 2 * per_op, kernels
+    return wall, 2 * per_op, kernels, parity
 
 
 def progress(msg):
@@ -345,8 +383,18 @@ def bench_f32b(mx, W, torch, reps):
     return out
 
 
-def bench_matmuls(mx, W, torch, reps):
+def bench_matmuls(mx, W, torch, reps, ref=None):
     out = {}
+    mref = ref["matmul"] if ref else {}
+
+    def attach(key, c_gpu_sample):
+        """Oracle timing and parity of one matmul part (c_gpu_sample: the
+        GPU's outputs at the oracle's sampled positions, on the host)."""
+        if key not in mref:
+            return
+        want, mag = mref[key]["ref"]
+        out[key]["cpu_oracle"] = mref[key]["cpu_oracle"]
+        out[key]["parity"] = t1_parity(c_gpu_sample, want, mag)
 
     # decode-shaped MXFP4 x MXFP4
     a, bt = W.decode_matmul_case()
@@ -378,6 +426,34 @@ def bench_matmuls(mx, W, torch, reps):
         "ms": round(cms, 5), "min_ms": round(cmn, 5), "achieved": round(cgbs, 1), "unit": "GB/s",
         "frac": round(cgbs / HBM_PEAK_GBS, 4),
         "what": "each call reads one of 40 weight copies (340 MB, beyond the Infinity Cache)"}
+    # The same launch shape reading the same bytes and writing C, with no
+    # arithmetic (bench_floor.hip): the memory floor of this launch, warm and
+    # with the weight read from HBM.
+    if os.path.exists(FLOOR_LIB):
+        import ctypes
+        fl = ctypes.CDLL(FLOOR_LIB)
+        fl.bench_read_floor.restype = ctypes.c_int
+        fl.bench_read_floor.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 3 + [ctypes.c_void_p]
+        def floor(w):
+            # the current stream at call time: under graph capture, the capturing one
+            stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            st = fl.bench_read_floor(at.codes.data_ptr(), at.scales.data_ptr(), w.codes.data_ptr(),
+                                     w.scales.data_ptr(), c.data_ptr(), 16, 4096, 4096, stream)
+            if st != 0:
+                raise RuntimeError(f"bench_read_floor failed ({st})")
+
+        fms, fmn = timed(torch, "floor", lambda: floor(btt), max(reps, 20))
+
+        def floor_cold():
+            k[0] = (k[0] + 1) % len(copies)
+            floor(copies[k[0]])
+        fcms, fcmn = timed(torch, "floor_cold", floor_cold, 40)
+        out["decode_mxfp4_16x4096x4096"]["read_floor"] = {
+            "ms": round(fms, 5), "cold_ms": round(fcms, 5),
+            "decode_over_floor": round(ms / fms, 3), "decode_cold_over_floor_cold": round(cms / fcms, 3),
+            "what": "same grid, same bytes read and C written, no decode or MFMA (bench_floor.hip)"}
+    mx.block_matmul(at, btt, out=c)
+    attach("decode_mxfp4_16x4096x4096", c.cpu().numpy())
     del at, btt, c, copies
 
     progress(f"decode-shaped matmul done: {ms:.4f} ms")
@@ -401,6 +477,10 @@ def bench_matmuls(mx, W, torch, reps):
         out["mxfp8_8192x8192x8192"]["sustained_clock_mhz"] = round(mhz)
         out["mxfp8_8192x8192x8192"]["frac_at_sustained_clock"] = round(
             tf / (PEAK_TFLOPS["fp8"] * mhz / 2400.0), 4)
+    if ref:
+        r, k = ref["rows"]["mxfp8"]
+        torch.cuda.synchronize()
+        attach("mxfp8_8192x8192x8192", c.cpu().numpy()[np.ix_(r, k)])
     del at, btt, c
     torch.cuda.empty_cache()
 
@@ -430,6 +510,11 @@ def bench_matmuls(mx, W, torch, reps):
         "roofline": {"bound": "mfma", "kernel": "block_matmul", "achieved": round(tfm, 1),
                      "peak": PEAK_TFLOPS["fp8"], "unit": "TFLOP/s",
                      "frac": round(tfm / PEAK_TFLOPS["fp8"], 4)}}
+    if ref:
+        prefill()
+        r, k = ref["rows"]["prefill"]
+        torch.cuda.synchronize()
+        attach("prefill_e4m3xe2m1_2048x28672x8192", c.cpu().numpy()[np.ix_(r, k)])
     del ad, btt, aq, c
     torch.cuda.empty_cache()
     return out
@@ -458,26 +543,154 @@ def bench_copy(torch, reps):
                     "context for the codec kernels' fractions"}
 
 
-def cpu_baseline(W, cols=8192, min_seconds=10.0):
-    """The oracle, as it stands, on the step's workload: whole 8192x8192
-    quantize + dequantize passes, repeated until at least `min_seconds` of CPU
-    time have elapsed (single-threaded NumPy)."""
+# --------------------------------------------------------------------------
+# CPU side: the oracle, timed on the host's cores, and the references the
+# bench line's parity entries are checked against.  All of it runs before
+# the GPU is first touched, so the worker pool forks a process that holds no
+# GPU state.
+# --------------------------------------------------------------------------
+_POOL_X = {}
+
+
+def _oracle_quantize_rows(job):
+    """Worker: oracle quantize (and optionally dequantize) of rows [r0, r1)
+    of the array registered under `name` before the pool forked."""
     from oracle import mx_oracle as O
-    x = W.weight_codec_case(8192, cols, seed=1002)
-    rows = x.shape[0]
+    name, r0, r1, elem, dequant, keep = job
+    x = _POOL_X[name][r0:r1]
+    c, s = O.quantize(x, elem)
+    y = O.dequantize(c, s, elem, x.shape[1]) if dequant else None
+    return (c, s, y) if keep else None
+
+
+def _row_jobs(name, rows, elem, parts, dequant=False, keep=True):
+    step = max(1, -(-rows // parts))
+    return [(name, r, min(rows, r + step), elem, dequant, keep) for r in range(0, rows, step)]
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max((d.get("num_threads") or 0) for d in threadpool_info()
+                   if d.get("user_api") == "blas") or None
+    except Exception:
+        return None
+
+
+def _time_matmul_oracle(O, args, min_seconds):
+    """The oracle's block_matmul, repeated for at least min_seconds; returns
+    (seconds per call, C, sum|ab|)."""
     t0 = time.perf_counter()
-    passes = 0
+    n = 0
     while True:
-        c, s = O.quantize(x, O.E2M1)
-        O.dequantize(c, s, O.E2M1, cols)
-        passes += 1
+        c, mag = O.block_matmul(*args)
+        n += 1
         dt = time.perf_counter() - t0
         if dt >= min_seconds:
-            break
-    gbs = passes * 2 * codec_bytes(rows, cols, 0.5) / dt / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{passes} quantize + dequantize pass(es) over the whole 8192x8192 "
-                      f"workload, single-threaded NumPy, {dt:.1f} s"}
+            return dt / n, c, mag
+
+
+def cpu_phase(W, codec_seconds=10.0, matmul_seconds=2.0):
+    """Oracle timings and parity references.
+
+    * Codec: whole quantize + dequantize passes of the 8192x8192 weight
+      workload, rows split over one worker process per available core (at
+      most 16, the CPU share of one GPU on the benchmark hosts), repeated for
+      at least codec_seconds.  The first pass is kept as the bit-exact
+      reference of the GPU step.
+    * Matmuls: the operands are quantized by the oracle (in the same pool) --
+      in full for the decode product, on a stated row sample of A and of B^T
+      for the MXFP8 and prefill products -- and the oracle's block_matmul
+      (float64 BLAS) is timed on them; its result is the reference of the
+      same outputs of the GPU product."""
+    import multiprocessing
+    from oracle import mx_oracle as O
+    avail = len(os.sched_getaffinity(0))
+    workers = max(1, min(avail, 16))
+    info = {"os_cpu_count": os.cpu_count(), "affinity_cores": avail, "workers": workers,
+            "cpu_model": _cpu_model()}
+    ref = {"info": info}
+    x = W.weight_codec_case(8192, 8192, seed=1002)
+    a3, bt3 = W.decode_matmul_case()
+    a4, bt4 = W.square_fp8_case()
+    a5, bt5 = W.prefill_linear_case()
+    rs = np.random.default_rng(7)
+    r4 = np.sort(rs.choice(8192, 512, replace=False)); c4 = np.sort(rs.choice(8192, 512, replace=False))
+    r5 = np.sort(rs.choice(2048, 256, replace=False)); c5 = np.sort(rs.choice(28672, 1024, replace=False))
+    _POOL_X.update(codec=x, a3=a3, bt3=bt3, a4=a4[r4], bt4=bt4[c4], a5=a5[r5], bt5=bt5[c5])
+    del a4, bt4, bt5
+    ctx = multiprocessing.get_context("fork")
+    with ctx.Pool(workers) as pool:
+        progress(f"CPU oracle: codec passes on {workers} worker processes")
+        jobs = _row_jobs("codec", 8192, O.E2M1, workers * 4, dequant=True)
+        t0 = time.perf_counter()
+        first = pool.map(_oracle_quantize_rows, jobs)
+        passes = 1
+        while time.perf_counter() - t0 < codec_seconds:
+            pool.map(_oracle_quantize_rows, [j[:5] + (False,) for j in jobs])
+            passes += 1
+        dt = time.perf_counter() - t0
+        ref["codec"] = tuple(np.concatenate([f[i] for f in first]) for i in range(3))
+        del first
+        gbs = passes * 2 * codec_bytes(8192, 8192, 0.5) / dt / 1e9
+        ref["cpu_baseline"] = {
+            "value": round(gbs, 4), "unit": "GB/s", "cores": workers, "kind": "oracle",
+            "sample": f"{passes} whole quantize + dequantize passes over the 8192x8192 MXFP4 "
+                      f"weight workload, rows split over {workers} worker processes "
+                      f"(one per available core, at most 16), {dt:.1f} s",
+            **info}
+        progress("CPU oracle: quantizing the matmul operands")
+        q = {}
+        for name, rows, elem in (("a3", 16, O.E2M1), ("bt3", 4096, O.E2M1), ("a4", 512, O.E4M3),
+                                 ("bt4", 512, O.E4M3), ("a5", 256, O.E4M3), ("bt5", 1024, O.E2M1)):
+            res = pool.map(_oracle_quantize_rows, _row_jobs(name, rows, elem, workers))
+            q[name] = (np.concatenate([r[0] for r in res]), np.concatenate([r[1] for r in res]))
+    _POOL_X.clear()
+    blas = _blas_threads()
+    mm = {}
+    for key, (an, bn, ae, be, K, what) in {
+            "decode_mxfp4_16x4096x4096": ("a3", "bt3", O.E2M1, O.E2M1, 4096, "every output"),
+            "mxfp8_8192x8192x8192": ("a4", "bt4", O.E4M3, O.E4M3, 8192,
+                                     "512 sampled rows of A x 512 sampled rows of B^T"),
+            "prefill_e4m3xe2m1_2048x28672x8192": ("a5", "bt5", O.E4M3, O.E2M1, 8192,
+                                                  "256 sampled rows of A x 1024 sampled rows of B^T")
+    }.items():
+        (ac, asc), (bc, bsc) = q[an], q[bn]
+        m, n = asc.shape[0], bsc.shape[0]
+        sec, c, mag = _time_matmul_oracle(O, (ac, asc, ae, bc, bsc, be, m, n, K), matmul_seconds)
+        flops = 2 * m * n * K
+        mm[key] = {"cpu_oracle": {"ms": round(sec * 1e3, 3), "tflops": round(flops / sec / 1e12, 4),
+                                  "blas_threads": blas, "kind": "oracle (float64 BLAS)",
+                                  "sample": what}, "ref": (c, mag)}
+    ref["matmul"] = mm
+    ref["rows"] = {"mxfp8": (r4, c4), "prefill": (r5, c5)}
+    progress("CPU oracle done")
+    return ref
+
+
+def t1_parity(got, want, mag):
+    """Worst |gpu - oracle| / (1e-5 sum|ab|) over the outputs, and whether
+    every output is within the stated tolerance (NaN positions equal)."""
+    got = got.astype(np.float64)
+    nan_ok = bool(np.array_equal(np.isnan(got), np.isnan(want)))
+    ok = ~np.isnan(want)
+    err = np.abs(got[ok] - want[ok].astype(np.float64))
+    bound = 1e-5 * mag[ok]
+    ratio = float(np.max(err / np.where(bound > 0, bound, 1.0))) if err.size else 0.0
+    within = nan_ok and bool(np.all(err <= bound))
+    return {"outputs": int(got.size), "worst_err_over_tolerance": round(ratio, 5),
+            "within_tolerance": within}
 
 
 def main():
@@ -498,9 +711,12 @@ def main():
               "measured on a single GPU", file=sys.stderr)
         sys.exit(2)
 
+    from bit_gemm_mx_amd import workloads as W
+    # The oracle runs first, on the host, before anything touches the GPU.
+    ref = None if args.no_cpu else cpu_phase(W)
+
     import torch
     import bit_gemm_mx_amd as mx
-    from bit_gemm_mx_amd import workloads as W
 
     if not os.path.exists(mx.binding.LIB_PATH):
         from bit_gemm_mx_amd.build import build
@@ -518,11 +734,12 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     if args.no_codec:
-        parts = bench_matmuls(mx, W, torch, max(3, args.steps // 2))
+        parts = bench_matmuls(mx, W, torch, max(3, args.steps // 2), ref)
         print(json.dumps({"metric": METRIC, "parts": parts, "note": "matmul workloads only"}))
         return
     progress("codec step: quantize + dequantize of the 8192x8192 weight workload")
-    wall, step_bytes, kernels = bench_codec(mx, W, torch, args.steps, args.warmup)
+    wall, step_bytes, kernels, codec_parity = bench_codec(mx, W, torch, args.steps, args.warmup,
+                                                          ref["codec"] if ref else None)
     progress(f"codec step done: {wall / args.steps * 1e3:.3f} ms/step")
     ms_step = wall / args.steps * 1e3
     value = step_bytes / (wall / args.steps) / 1e9
@@ -530,7 +747,7 @@ def main():
     dominant = max(kernels, key=lambda k: kernels[k]["ms"])
     parts = {"codec_kernels": rooflines}
     if not args.no_matmul:
-        parts.update(bench_matmuls(mx, W, torch, max(3, args.steps // 2)))
+        parts.update(bench_matmuls(mx, W, torch, max(3, args.steps // 2), ref))
         parts.update(bench_f32b(mx, W, torch, max(3, args.steps // 2)))
     parts.update(bench_axis0_fold(mx, W, torch, max(3, args.steps // 2)))
     parts.update(bench_roundtrip(mx, W, torch, max(3, args.steps // 2)))
@@ -546,11 +763,11 @@ def main():
                    "rows": 8192, "cols": 8192, "elem": "E2M1", "block_size": 32, "seed": 1002,
                    "step": "mx_quantize then mx_dequantize"},
         "roofline": rooflines[dominant],
+        "parity": codec_parity,
         "parts": parts,
     }
-    if not args.no_cpu:
-        progress("timing the CPU oracle on a sample")
-        line["cpu_baseline"] = cpu_baseline(W)
+    if ref:
+        line["cpu_baseline"] = ref["cpu_baseline"]
     print(json.dumps(line), flush=True)
 
 
