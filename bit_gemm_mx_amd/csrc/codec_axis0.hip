@@ -64,29 +64,21 @@ __device__ __forceinline__ void load_block(float (&v)[32], const float* __restri
 }
 
 template <int ELEM>
-__global__ void __launch_bounds__(kThreads)
-quantize_axis0_kernel(const float* __restrict__ x, uint8_t* __restrict__ codes,
-                      uint8_t* __restrict__ scales, int64_t rows, int64_t cols, int scale_vec) {
-  using F = Fmt<ELEM>;
-  const Task k = task_of(cols);
-  const int64_t nbr = rows / 32;
-  if (k.i0 >= nbr) return;  // wave-uniform: past the last run of the strip
-  const int run = (int)min((int64_t)kRun, nbr - k.i0);
-  const int64_t row_bytes = ELEM == kE2M1 ? rows / 2 : rows;
-  constexpr int kBlockBytes = ELEM == kE2M1 ? 16 : 32;
-  uint8_t* crow = codes + k.ca * row_bytes;
-  uint8_t* srow = scales + k.ca * nbr;
+struct Run {
+  static constexpr int kBlockBytes = ELEM == kE2M1 ? 16 : 32;  // codes of one block
+  static constexpr int kVecs = kBlockBytes / 16;
+  u4v codes[kRun][kVecs];  // the run's codes, kRun x kBlockBytes contiguous bytes
+  uint32_t bytes[kRun];    // the run's scale bytes
+};
 
-  uint32_t sbytes[kRun / 4] = {};
-  // The run's codes are kept in registers and stored together at the end:
-  // kRun x 16 (E2M1) or 32 (E4M3) contiguous bytes per lane (64 or 128), half
-  // or whole cache lines, instead of one 16-byte piece of a line per
-  // block-row.
-  constexpr int kVecs = kBlockBytes / 16;
-  u4v cbuf[kRun][kVecs];
-  // Block-rows are loaded kPf ahead of the one being encoded, into a ring of
-  // kPf + 1 register buffers indexed at compile time (measured: one block
-  // ahead 65 us, two 62.5 us, three no better, for the 8192x8192 E2M1 case).
+// Encode the run of block-rows [k.i0, k.i0 + run) of this lane's column.
+// Block-rows are loaded kPf ahead of the one being encoded, into a ring of
+// kPf + 1 register buffers indexed at compile time (measured: one block
+// ahead 65 us, two 62.5 us, three no better, for the 8192x8192 E2M1 case).
+template <int ELEM>
+__device__ __forceinline__ void encode_run(Run<ELEM>& out, const float* __restrict__ x,
+                                           int64_t cols, const Task& k, int run) {
+  using F = Fmt<ELEM>;
   constexpr int kPf = 2;
   float vb[kPf + 1][32];
 #pragma unroll
@@ -94,6 +86,7 @@ quantize_axis0_kernel(const float* __restrict__ x, uint8_t* __restrict__ codes,
     if (r < run) load_block(vb[r], x, k.i0 + r, cols, k);
 #pragma unroll
   for (int r = 0; r < kRun; ++r) {
+    out.bytes[r] = 127u;
     if (r >= run) break;  // wave-uniform
     if (r + kPf < run) load_block(vb[(r + kPf) % (kPf + 1)], x, k.i0 + r + kPf, cols, k);
     const float* v = vb[r % (kPf + 1)];
@@ -106,7 +99,7 @@ quantize_axis0_kernel(const float* __restrict__ x, uint8_t* __restrict__ codes,
     }
     const int e = block_exponent<ELEM>(amax);
     const bool nonfinite = amax >= 0x7F800000u;
-    const uint32_t byte = amax == 0 ? 127u : (nonfinite ? 0xFFu : (uint32_t)(e + 127));
+    out.bytes[r] = amax == 0 ? 127u : (nonfinite ? 0xFFu : (uint32_t)(e + 127));
     const float inv_scale = __uint_as_float((uint32_t)(127 - e) << 23);
     const float scale = __uint_as_float((uint32_t)max(e + 127, 1) << 23);
     const bool exact = k.live && (low == 0 || amax < 0x0D800000u);
@@ -128,32 +121,107 @@ quantize_axis0_kernel(const float* __restrict__ x, uint8_t* __restrict__ codes,
       for (int q = 0; q < 8; ++q) w[q] = 0;
     }
     if (ELEM == kE2M1) {
-      cbuf[r][0] = u4v{w[0] | (w[1] << 16), w[2] | (w[3] << 16), w[4] | (w[5] << 16),
-                       w[6] | (w[7] << 16)};
+      out.codes[r][0] = u4v{w[0] | (w[1] << 16), w[2] | (w[3] << 16), w[4] | (w[5] << 16),
+                            w[6] | (w[7] << 16)};
     } else {
-      cbuf[r][0] = u4v{w[0], w[1], w[2], w[3]};
-      cbuf[r][kVecs - 1] = u4v{w[4], w[5], w[6], w[7]};
-    }
-    if (k.live) {
-      if (scale_vec)
-        sbytes[r >> 2] |= byte << (8 * (r & 3));
-      else
-        srow[k.i0 + r] = (uint8_t)byte;
+      out.codes[r][0] = u4v{w[0], w[1], w[2], w[3]};
+      out.codes[r][Run<ELEM>::kVecs - 1] = u4v{w[4], w[5], w[6], w[7]};
     }
   }
-  if (k.live) {
+}
+
+// One wave per (64-column strip, run of kRun block-rows); each lane stores
+// its run's codes (kRun x 16 or 32 contiguous bytes, half or whole cache
+// lines) and scale bytes itself.  Any row count and scale alignment.
+template <int ELEM>
+__global__ void __launch_bounds__(kThreads)
+quantize_axis0_kernel(const float* __restrict__ x, uint8_t* __restrict__ codes,
+                      uint8_t* __restrict__ scales, int64_t rows, int64_t cols, int scale_vec) {
+  const Task k = task_of(cols);
+  const int64_t nbr = rows / 32;
+  if (k.i0 >= nbr) return;  // wave-uniform: past the last run of the strip
+  const int run = (int)min((int64_t)kRun, nbr - k.i0);
+  const int64_t row_bytes = ELEM == kE2M1 ? rows / 2 : rows;
+  constexpr int kBlockBytes = Run<ELEM>::kBlockBytes, kVecs = Run<ELEM>::kVecs;
+  Run<ELEM> o;
+  encode_run<ELEM>(o, x, cols, k, run);
+  if (!k.live) return;
+  uint8_t* crow = codes + k.c * row_bytes;
+  uint8_t* srow = scales + k.c * nbr;
 #pragma unroll
-    for (int r = 0; r < kRun; ++r) {
-      if (r < run) {
+  for (int r = 0; r < kRun; ++r) {
+    if (r < run) {
 #pragma unroll
-        for (int h = 0; h < kVecs; ++h)
-          *reinterpret_cast<u4v*>(crow + (k.i0 + r) * kBlockBytes + 16 * h) = cbuf[r][h];
-      }
+      for (int h = 0; h < kVecs; ++h)
+        *reinterpret_cast<u4v*>(crow + (k.i0 + r) * kBlockBytes + 16 * h) = o.codes[r][h];
+      if (!scale_vec) srow[k.i0 + r] = (uint8_t)o.bytes[r];
     }
   }
   // Whole runs with 4-byte aligned scale rows: one store of the run's bytes.
-  if (scale_vec && k.live)
-    *reinterpret_cast<uint32_t*>(srow + k.i0) = sbytes[0];
+  if (scale_vec)
+    *reinterpret_cast<uint32_t*>(srow + k.i0) =
+        o.bytes[0] | (o.bytes[1] << 8) | (o.bytes[2] << 16) | (o.bytes[3] << 24);
+}
+
+// The eight waves of a workgroup take eight consecutive runs (32 block-rows)
+// of the same 64-column strip, then store through LDS: each column's codes
+// for the 32 block-rows are 512 (E2M1) or 1024 (E4M3) contiguous bytes and
+// its 32 scale bytes are contiguous too, so every store instruction writes
+// whole cache lines of a few columns instead of a 64-byte piece (and a
+// 4-byte scale piece) of 64 columns 4 KiB apart.  With the stores removed
+// the 8192x8192 E2M1 quantize reads its input in 46 us; the per-lane
+// stores cost 16 us more, these 11 (four waves per workgroup and 256-byte
+// pieces: 14; sixteen waves and 1 KiB pieces: 10).  Workgroups walk all
+// strips of a row range before the next (bands of 4..32 strips down all
+// rows measured 68-73 us).  Needs rows % 1024 == 0 and 16-byte aligned
+// scale rows.
+constexpr int kGroupRuns = 8;  // runs per workgroup
+constexpr int kStagedThreads = 64 * kGroupRuns;
+
+template <int ELEM>
+__global__ void __launch_bounds__(kStagedThreads)
+quantize_axis0_staged_kernel(const float* __restrict__ x, uint8_t* __restrict__ codes,
+                             uint8_t* __restrict__ scales, int64_t rows, int64_t cols) {
+  constexpr int kBlockBytes = Run<ELEM>::kBlockBytes, kVecs = Run<ELEM>::kVecs;
+  constexpr int kColBytes = kGroupRuns * kRun * kBlockBytes;  // one column's codes here
+  constexpr int kStride = kColBytes + 16;                     // padded LDS row
+  __shared__ __attribute__((aligned(16))) uint8_t lds_codes[64 * kStride];
+  __shared__ __attribute__((aligned(16))) uint32_t lds_scales[64 * kGroupRuns];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t n_strips = (cols + 63) / 64;
+  const int64_t strip = blockIdx.x % n_strips, group = blockIdx.x / n_strips;
+  Task k;
+  k.c = strip * 64 + lane;
+  k.live = k.c < cols;
+  k.ca = k.live ? k.c : cols - 1;
+  k.i0 = (group * kGroupRuns + wave) * kRun;
+  Run<ELEM> o;
+  encode_run<ELEM>(o, x, cols, k, kRun);
+#pragma unroll
+  for (int r = 0; r < kRun; ++r)
+#pragma unroll
+    for (int h = 0; h < kVecs; ++h)
+      *reinterpret_cast<u4v*>(lds_codes + lane * kStride + (wave * kRun + r) * kBlockBytes +
+                              16 * h) = o.codes[r][h];
+  lds_scales[lane * kGroupRuns + wave] =
+      o.bytes[0] | (o.bytes[1] << 8) | (o.bytes[2] << 16) | (o.bytes[3] << 24);
+  __syncthreads();
+  const int64_t row_bytes = ELEM == kE2M1 ? rows / 2 : rows;
+  const int64_t c0 = strip * 64, b0 = group * kGroupRuns * kRun;  // first column, block-row
+  constexpr int kChunks = kColBytes / 16;                         // 16-byte chunks per column
+  constexpr int kColsPerPass = kStagedThreads / kChunks;
+#pragma unroll
+  for (int p = 0; p < 64 / kColsPerPass; ++p) {
+    const int col = p * kColsPerPass + threadIdx.x / kChunks, ch = threadIdx.x % kChunks;
+    if (c0 + col < cols)
+      *reinterpret_cast<u4v*>(codes + (c0 + col) * row_bytes + b0 * kBlockBytes + 16 * ch) =
+          *reinterpret_cast<const u4v*>(lds_codes + col * kStride + 16 * ch);
+  }
+  // 32 scale bytes per column: two 16-byte stores
+  const int sc = threadIdx.x / 2, half = threadIdx.x & 1;
+  if (threadIdx.x < 128 && c0 + sc < cols)
+    *reinterpret_cast<u4v*>(scales + (c0 + sc) * (rows / 32) + b0 + 16 * half) =
+        *reinterpret_cast<const u4v*>(lds_scales + sc * kGroupRuns + 4 * half);
 }
 
 template <int ELEM>
@@ -237,10 +305,22 @@ Launch plan(const uint8_t* scales, int64_t rows, int64_t cols) {
 
 hipError_t launch_quantize_axis0(const float* x, void* codes, uint8_t* scales, int64_t rows,
                                  int64_t cols, int elem, hipStream_t stream) {
+  uint8_t* c = static_cast<uint8_t*>(codes);
+  if (rows % (32 * kRun * kGroupRuns) == 0 && (reinterpret_cast<uintptr_t>(scales) & 15) == 0) {
+    const int64_t groups = rows / (32 * kRun * kGroupRuns), strips = (cols + 63) / 64;
+    if (groups * strips > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(groups * strips));
+    if (elem == kE2M1)
+      hipLaunchKernelGGL(quantize_axis0_staged_kernel<kE2M1>, grid, dim3(kStagedThreads), 0,
+                         stream, x, c, scales, rows, cols);
+    else
+      hipLaunchKernelGGL(quantize_axis0_staged_kernel<kE4M3>, grid, dim3(kStagedThreads), 0,
+                         stream, x, c, scales, rows, cols);
+    return hipGetLastError();
+  }
   const Launch l = plan(scales, rows, cols);
   if (l.grid.x == 0 || (int64_t)l.grid.x * (kThreads / 64) < ((cols + 63) / 64) * l.n_runs)
     return hipErrorInvalidValue;
-  uint8_t* c = static_cast<uint8_t*>(codes);
   if (elem == kE2M1)
     hipLaunchKernelGGL(quantize_axis0_kernel<kE2M1>, l.grid, dim3(kThreads), 0, stream, x, c,
                        scales, rows, cols, l.scale_vec);

@@ -39,7 +39,7 @@ def gpu_quantize_axis0(x, elem):
 
 @pytest.mark.parametrize("elem", ELEMS)
 @pytest.mark.parametrize("rows,cols", [(32, 1), (32, 64), (64, 100), (96, 130), (256, 64),
-                                        (288, 200), (512, 96), (1024, 33)])
+                                        (288, 200), (512, 96), (1024, 33), (2048, 130)])
 def test_quantize_axis0_bit_exact(elem, rows, cols):
     rng = np.random.default_rng(rows * 7 + cols + elem)
     x = spread_normal(rng, rows, cols)
@@ -134,6 +134,27 @@ def test_axis0_unaligned_scales_and_guards(elem):
     assert_bits_equal(yb[4:4 + rows * cols].reshape(rows, cols),
                       O.dequantize_axis0(oc, os_, elem, rows), "dequantize")
     assert (yb[:4] == -7.0).all() and (yb[4 + rows * cols:] == -7.0).all()
+
+
+@pytest.mark.parametrize("elem", ELEMS)
+@pytest.mark.parametrize("rows,cols", [(1024, 70), (3072, 129)])
+def test_axis0_staged_stores_and_guards(elem, rows, cols):
+    # rows a multiple of 1024 with 16-byte aligned scales: the workgroup-staged
+    # store path, ragged last strip; guard bytes around codes and scales
+    rng = np.random.default_rng(rows + cols + elem)
+    x = spread_normal(rng, rows, cols)
+    oc, os_ = O.quantize_axis0(x, elem)
+    cbuf = torch.full((oc.size + 64,), 0xA5, dtype=torch.uint8, device="cuda")
+    sbuf = torch.full((os_.size + 64,), 0x5A, dtype=torch.uint8, device="cuda")
+    xd = dev(x)
+    cptr, sptr = cbuf.data_ptr() + 16, sbuf.data_ptr() + 16
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    B.mx_quantize_axis(xd.data_ptr(), cptr, sptr, rows, cols, 0, elem, 32, stream)
+    cb, sb = host(cbuf), host(sbuf)
+    assert_bits_equal(cb[16:16 + oc.size].reshape(oc.shape), oc, "codes")
+    assert_bits_equal(sb[16:16 + os_.size].reshape(os_.shape), os_, "scales")
+    assert (cb[:16] == 0xA5).all() and (cb[16 + oc.size:] == 0xA5).all()
+    assert (sb[:16] == 0x5A).all() and (sb[16 + os_.size:] == 0x5A).all()
 
 
 def test_axis0_weight_workload_full():
