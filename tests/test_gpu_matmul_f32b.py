@@ -4,8 +4,9 @@ float32 B) against the oracle.
 Bound, per output element: |gpu - oracle| <= 1e-5 * sum_k |a_k b_k|
 (+ |C_in| when accumulating), the matmul tolerance of the quantized path,
 with identical NaN positions and exact zeros where the bound is 0.  Shapes
-cover both launch shapes (16x16 tiles with K split over the waves; 128x64
-tiles), ragged M, N and K, and the two measured workloads in full: decode
+cover every launch shape (16x16 tiles with K split over the waves, operands
+loaded element-wise or streamed through LDS; 128x64 tiles), ragged M, N and
+K, a B that is not 16-byte aligned, and the two measured workloads in full: decode
 (MXFP4 weights 4096x4096 times float32 activations 4096x16) and the square
 4096^3 product.
 """
@@ -48,10 +49,15 @@ def run(ac, asc, elem, b, M, N, K, c_in=None, accumulate=False):
 SHAPES = [(1, 1, 32), (3, 5, 64), (16, 16, 128), (17, 33, 160), (70, 100, 1056), (5, 7, 8192),
           (300, 520, 2048), (1024, 1024, 512), (1030, 1100, 320), (64, 2048, 96),
           (2100, 1100, 320), (2048, 2048, 1024)]
+# Shapes for the streamed K-split launch (K % 256 == 0, N % 4 == 0, few tiles):
+# one 256-K unit (15 of 16 waves idle), units not a multiple of 16, ragged M,
+# N = 4 and column tiles cut short of 16, the decode shape's K at small M.
+STREAM_SHAPES = [(1, 4, 256), (17, 20, 256), (33, 4, 4352), (100, 36, 8448), (5, 12, 4096),
+                 (130, 68, 1280)]
 
 
 @pytest.mark.parametrize("elem", ELEMS)
-@pytest.mark.parametrize("M,N,K", SHAPES)
+@pytest.mark.parametrize("M,N,K", SHAPES + STREAM_SHAPES)
 def test_random_operands(elem, M, N, K):
     rng = np.random.default_rng(M * 131 + N * 7 + K + elem)
     ac, asc = rand_a(rng, M, K, elem)
@@ -76,7 +82,7 @@ def test_quantized_float_weights(elem):
 
 
 @pytest.mark.parametrize("elem", ELEMS)
-@pytest.mark.parametrize("M,N,K", [(20, 30, 96), (1100, 300, 256)])
+@pytest.mark.parametrize("M,N,K", [(20, 30, 96), (1100, 300, 256), (40, 20, 1024)])
 def test_accumulate(elem, M, N, K):
     rng = np.random.default_rng(M + N + K)
     ac, asc = rand_a(rng, M, K, elem)
@@ -184,4 +190,22 @@ def test_square_4096_full():
     del a
     torch.cuda.empty_cache()
     want, mag = O.block_matmul_f32b(ac, asc, O.E2M1, x, 4096, 4096, 4096)
+    assert_matmul_close(got, want, mag)
+
+
+@pytest.mark.parametrize("elem", ELEMS)
+def test_b_not_16_byte_aligned(elem):
+    """A B that starts 4 bytes past a 16-byte boundary cannot take the streamed
+    launch's 16-byte loads; the call must still give the oracle's result."""
+    rng = np.random.default_rng(11)
+    M, N, K = 64, 16, 1024
+    ac, asc = rand_a(rng, M, K, elem)
+    b = rand_b(rng, K, N)
+    buf = torch.zeros(K * N + 4, dtype=torch.float32, device="cuda")
+    bd = buf[1:1 + K * N].view(K, N)
+    bd.copy_(dev(b))
+    assert bd.data_ptr() % 16 == 4
+    a = B.MXTensor(dev(ac), dev(asc), M, K, elem)
+    got = host(B.block_matmul_f32b(a, bd))
+    want, mag = O.block_matmul_f32b(ac, asc, elem, b, M, N, K)
     assert_matmul_close(got, want, mag)
