@@ -157,6 +157,33 @@ def test_axis0_staged_stores_and_guards(elem, rows, cols):
     assert (sb[:16] == 0x5A).all() and (sb[16 + os_.size:] == 0x5A).all()
 
 
+@pytest.mark.parametrize("elem", ELEMS)
+@pytest.mark.parametrize("rows,cols", [(1024, 68), (2048, 260), (1024, 512), (3072, 1028)])
+def test_axis0_staged_column_counts_and_special_values(elem, rows, cols):
+    # the workgroup-staged store path at column counts that end inside a
+    # 64-column strip (68, 260, 1028) or on one (512), with special values in
+    # the first and the last block-rows, and guard bytes around the outputs
+    rng = np.random.default_rng(rows + 3 * cols + elem)
+    x = spread_normal(rng, rows, cols)
+    x[:6, 1] = [6.0, 0.75, -0.75, 1.75, 3.5, -0.0]     # grid ties of E2M1
+    x[32:64, 2] = -0.0
+    x[64, 3] = np.nan
+    x[rows - 32, cols - 1] = np.inf
+    x[rows - 31:, cols - 2] = 2.0 ** -140              # f32 subnormal block maximum
+    oc, os_ = O.quantize_axis0(x, elem)
+    cbuf = torch.full((oc.size + 64,), 0xA5, dtype=torch.uint8, device="cuda")
+    sbuf = torch.full((os_.size + 64,), 0x5A, dtype=torch.uint8, device="cuda")
+    xd = dev(x)
+    cptr, sptr = cbuf.data_ptr() + 16, sbuf.data_ptr() + 16
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    B.mx_quantize_axis(xd.data_ptr(), cptr, sptr, rows, cols, 0, elem, 32, stream)
+    cb, sb = host(cbuf), host(sbuf)
+    assert_bits_equal(cb[16:16 + oc.size].reshape(oc.shape), oc, "codes")
+    assert_bits_equal(sb[16:16 + os_.size].reshape(os_.shape), os_, "scales")
+    assert (cb[:16] == 0xA5).all() and (cb[16 + oc.size:] == 0xA5).all()
+    assert (sb[:16] == 0x5A).all() and (sb[16 + os_.size:] == 0x5A).all()
+
+
 def test_axis0_weight_workload_full():
     """The 8192x8192 MXFP4 weight workload blocked along axis 0: every code,
     scale and dequantized element."""
