@@ -50,6 +50,8 @@ def lib() -> ctypes.CDLL:
     L.mx_block_matmul.restype = i32
     L.mx_block_matmul_f32b.argtypes = [p, p, i32, p, p, i64, i64, i64, i32, i32, p]
     L.mx_block_matmul_f32b.restype = i32
+    L.mx_block_matmul_quantize_a.argtypes = [p, i32, p, p, i32, p, i64, i64, i64, i32, i32, p]
+    L.mx_block_matmul_quantize_a.restype = i32
     L.mx_quantize_axis.argtypes = [p, p, p, i64, i64, i32, i32, i32, p]
     L.mx_quantize_axis.restype = i32
     L.mx_dequantize_axis.argtypes = [p, p, p, i64, i64, i32, i32, i32, p]
@@ -108,6 +110,12 @@ def mx_block_matmul_f32b(a_codes, a_scales, a_elem, b, c, M, N, K, block_size=BL
                          accumulate=0, stream=None):
     _check(lib().mx_block_matmul_f32b(a_codes, a_scales, a_elem, b, c, M, N, K, block_size,
                                       accumulate, stream))
+
+
+def mx_block_matmul_quantize_a(a, a_elem, b_codes, b_scales, b_elem, c, M, N, K,
+                               block_size=BLOCK, accumulate=0, stream=None):
+    _check(lib().mx_block_matmul_quantize_a(a, a_elem, b_codes, b_scales, b_elem, c, M, N, K,
+                                            block_size, accumulate, stream))
 
 
 def mx_codes_bytes(rows, cols, elem) -> int:
@@ -300,4 +308,34 @@ def block_matmul_f32b(a: MXTensor, b, out=None, accumulate: bool = False):
     mx_block_matmul_f32b(a.codes.data_ptr(), a.scales.data_ptr(), a.elem, b.data_ptr(),
                          out.data_ptr(), M, N, K, BLOCK, 1 if accumulate else 0,
                          _stream_ptr(out.device))
+    return out
+
+
+def block_matmul_quantize_a(a, a_elem: int, bt: MXTensor, out=None, accumulate: bool = False):
+    """C = [C +] Q(A) . B with A an ordinary float32 [M, K] GPU tensor,
+    quantized along K to a_elem inside the product exactly as quantize()
+    would, and B given as B^T [N, K] blocked along its last axis or as B
+    [K, N] blocked along axis 0 (mx_block_matmul_quantize_a)."""
+    import torch
+    if not isinstance(a, torch.Tensor) or a.dim() != 2:
+        raise ValueError("A must be a 2-D float32 tensor [M, K]")
+    bn, bk = (bt.rows, bt.cols) if bt.axis == 1 else (bt.cols, bt.rows)
+    M, K = a.shape
+    if K != bk:
+        raise ValueError(f"K mismatch: A has {K}, B has {bk}")
+    N = bn
+    _require(a, torch.float32, "a", shape=(M, K), on_gpu=False)
+    _require_mx(bt, "bt", on_gpu=False)
+    if out is not None:
+        _require(out, torch.float32, "out", shape=(M, N), on_gpu=False)
+    _require(a, torch.float32, "a", shape=(M, K))
+    _require_mx(bt, "bt", device=a.device)
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs an existing out tensor")
+        out = torch.empty((M, N), dtype=torch.float32, device=a.device)
+    _require(out, torch.float32, "out", shape=(M, N), device=a.device)
+    mx_block_matmul_quantize_a(a.data_ptr(), a_elem, bt.codes.data_ptr(), bt.scales.data_ptr(),
+                               bt.elem, out.data_ptr(), M, N, K, BLOCK, 1 if accumulate else 0,
+                               _stream_ptr(out.device))
     return out

@@ -26,6 +26,7 @@
 #include <type_traits>
 #include <utility>
 
+#include "codec_common.h"
 #include "mx_internal.h"
 
 namespace mx {
@@ -796,6 +797,267 @@ hipError_t launch_skinny(const uint8_t* a, const uint8_t* sa, const uint8_t* b,
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Fused activation quantize + matmul: C[M,N] (+)= Q(A) . B^T with A float32
+// [M, K] and Q the last-axis MX quantize of mx_quantize (same block
+// exponent, same element rounding, same codes: the encode of codec_common.h),
+// B^T [N, K] block-scaled.  The quantized A never leaves the chip: each K
+// stage of 128 loads the tile's float32 A rows, quantizes them in registers
+// and writes codes and scale bytes into the LDS stage that the MFMAs read,
+// in the layout of the tiled kernel (so its operand reads, the exact split of
+// an E4M3 operand against E2M1, and its epilogue apply unchanged).
+//
+// Tiles of 128 x 128, 4 waves of 64 x 64 (2 x 2 MFMA tiles of 32x32x64).
+// Two LDS stages: stage st + 1's global loads are issued before stage st's
+// MFMAs and quantized after them.  A's rows are read (and quantized) once per
+// tile column, i.e. N / 128 times over: the price of not storing Q(A).
+//
+// A loads: wave w covers rows 32w .. 32w + 31 of the tile, two rows per
+// 16-byte load instruction (lane l: row 2i + l / 32, floats 4 (l % 32) .. + 3
+// of the stage), so one instruction reads two contiguous 512-byte row pieces
+// and each aligned group of 8 lanes holds one 32-element block, whose amax is
+// reduced across the 8 lanes as in the quantize kernel.
+// ---------------------------------------------------------------------------
+constexpr int kFusedTM = 128, kFusedTN = 128, kFusedTK = 128;
+constexpr int kFusedThreads = 256;
+
+// Max of v over each aligned group of 8 lanes.
+__device__ __forceinline__ uint32_t max_over_8_lanes(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // lane ^ 1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // lane ^ 2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // 7 - lane
+  return v;
+}
+
+template <int AE, int BE>
+struct FusedStage {
+  static constexpr int kA = Stage<AE, kFusedTK, 4, kFusedTM>::kBytes;  // A codes
+  static constexpr int kB = Stage<BE, kFusedTK, 4, kFusedTN>::kBytes;  // B^T codes
+  static constexpr int kBytes = kA + kB + 4 * (kFusedTM + kFusedTN);   // + a scale dword per row
+  static constexpr int kBChunks = Stage<BE, kFusedTK>::kChunks;        // 16-byte chunks per row
+  static constexpr int kBPieces = kB / 16 / kFusedThreads;             // per thread
+};
+
+template <int AE, int BE>
+__global__ void __launch_bounds__(kFusedThreads)
+block_matmul_quant_a(const float* __restrict__ a, const uint8_t* __restrict__ b,
+                     const uint8_t* __restrict__ sb, float* __restrict__ c, int64_t M, int64_t N,
+                     int64_t K, int accumulate, int tiles_m, int tiles_n) {
+  using FS = FusedStage<AE, BE>;
+  using F = codec::Fmt<AE>;
+  constexpr int kMQ = 2, kNQ = 2;  // 32x32 MFMA tiles per wave
+  __shared__ __attribute__((aligned(1024))) uint8_t smem0[FS::kBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem1[FS::kBytes];
+
+  // Tile order as in the tiled kernel: a contiguous range of tiles per XCD,
+  // walked in groups of up to 8 tile-rows.
+  const int nwg = tiles_m * tiles_n;
+  int pid = blockIdx.x;
+  if ((nwg & 7) == 0) pid = (pid & 7) * (nwg >> 3) + (pid >> 3);
+  constexpr int kGroup = 8;
+  const int in_group = kGroup * tiles_n;
+  const int first_m = (pid / in_group) * kGroup;
+  const int gsize = min(tiles_m - first_m, kGroup);
+  const int tm = first_m + (pid % in_group) % gsize;
+  const int tn = (pid % in_group) / gsize;
+  const int64_t m0 = (int64_t)tm * kFusedTM, n0 = (int64_t)tn * kFusedTN;
+
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = wave >> 1, wn = wave & 1, g = lane >> 5, lr = lane & 31;
+  const int64_t kblocks = K / 32;
+  const int stages = (int)((K + kFusedTK - 1) / kFusedTK);
+  constexpr int kBRowBytes = Stage<BE, kFusedTK>::kRowBytes;      // per stage
+  const int64_t b_row_bytes = BE == kE2M1 ? K / 2 : K;
+  constexpr int kBChunkK = BE == kE2M1 ? 32 : 16;                 // K elements per chunk
+
+  const int acol = 4 * (lane & 31);  // this lane's first float of a stage row
+  float4 av[16];
+  uint4 bv[FS::kBPieces];
+  uint32_t bsv = 0x7F7F7F7Fu;
+
+  auto load = [&](int st) {
+    const int64_t k = (int64_t)st * kFusedTK + acol;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int64_t row = min(m0 + 32 * wave + 2 * i + (lane >> 5), M - 1);
+      av[i] = k < K ? *reinterpret_cast<const float4*>(a + row * K + k)
+                    : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int p = 0; p < FS::kBPieces; ++p) {
+      const int P = p * kFusedThreads + t;
+      const int row = P / FS::kBChunks, ch = P % FS::kBChunks;
+      const int64_t grow = n0 + row;
+      const bool ok = grow < N && (int64_t)st * kFusedTK + ch * kBChunkK < K;
+      bv[p] = ok ? *reinterpret_cast<const uint4*>(b + grow * b_row_bytes +
+                                                   (int64_t)st * kBRowBytes + 16 * ch)
+                 : make_uint4(0u, 0u, 0u, 0u);
+    }
+    if (t < kFusedTN) {
+      // Blocks past K or rows past N get scale 2^0 (their codes are zero; a
+      // 0xFF byte would poison the row in the MFMA).
+      uint32_t w = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t kb = 4 * (int64_t)st + j;
+        const uint32_t byte = (n0 + t < N && kb < kblocks) ? sb[(n0 + t) * kblocks + kb] : 127u;
+        w |= byte << (8 * j);
+      }
+      bsv = w;
+    }
+  };
+
+  auto store = [&](int st, uint8_t* buf) {
+    uint8_t* la = buf;
+    uint8_t* lb = buf + FS::kA;
+    uint32_t* lsa = reinterpret_cast<uint32_t*>(buf + FS::kA + FS::kB);
+    uint32_t* lsb = lsa + kFusedTM;
+    const bool k_live = (int64_t)st * kFusedTK + acol < K;
+    uint32_t amax[16], low = 0xFFFFFFFFu;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t b0 = __float_as_uint(av[i].x), b1 = __float_as_uint(av[i].y);
+      const uint32_t b2 = __float_as_uint(av[i].z), b3 = __float_as_uint(av[i].w);
+      amax[i] = max(max(b0 & 0x7FFFFFFFu, b1 & 0x7FFFFFFFu), max(b2 & 0x7FFFFFFFu, b3 & 0x7FFFFFFFu));
+      const bool live = k_live && m0 + 32 * wave + 2 * i + (lane >> 5) < M;
+      if (live)
+        low = min(low, min(min(b0 << F::kTieShift, b1 << F::kTieShift),
+                           min(b2 << F::kTieShift, b3 << F::kTieShift)));
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax[i] = max_over_8_lanes(amax[i]);
+    bool exact = low == 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) exact |= amax[i] < 0x0D800000u;
+    const bool fast = __ballot(exact) == 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 32 * wave + 2 * i + (lane >> 5);  // row within the tile
+      const uint32_t am = amax[i];
+      const int e = codec::block_exponent<AE>(am);
+      const bool nonfinite = am >= 0x7F800000u;
+      const uint32_t byte = am == 0 ? 127u : (nonfinite ? 0xFFu : (uint32_t)(e + 127));
+      const float scale = __uint_as_float((uint32_t)max(e + 127, 1) << 23);
+      const float inv_scale = __uint_as_float((uint32_t)(127 - e) << 23);
+      uint32_t w = fast ? codec::convert4<AE>(av[i], scale, AE == kE4M3 ? 448.0f * scale : 0.0f)
+                        : codec::round4<AE>(av[i], inv_scale);
+      w = nonfinite ? 0u : w;
+      if (AE == kE4M3)
+        *reinterpret_cast<uint32_t*>(la + lds_off<AE, kFusedTK>(r, acol >> 4) + (acol & 15)) = w;
+      else
+        *reinterpret_cast<uint16_t*>(la + lds_off<AE, kFusedTK>(r, acol >> 5) +
+                                     ((acol >> 1) & 15)) = (uint16_t)w;
+      if ((lane & 7) == 0) buf[FS::kA + FS::kB + 4 * r + ((lane & 31) >> 3)] = (uint8_t)byte;
+    }
+#pragma unroll
+    for (int p = 0; p < FS::kBPieces; ++p) {
+      const int P = p * kFusedThreads + t;
+      *reinterpret_cast<uint4*>(lb + lds_off<BE, kFusedTK>(P / FS::kBChunks, P % FS::kBChunks)) =
+          bv[p];
+    }
+    if (t < kFusedTN) lsb[t] = bsv;
+    (void)lsa;
+  };
+
+  v16f acc[kMQ][kNQ];
+#pragma unroll
+  for (int i = 0; i < kMQ; ++i)
+#pragma unroll
+    for (int j = 0; j < kNQ; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  const int ar = wm * 64 + lr, br = wn * 64 + lr;
+
+  auto mfma = [&](const uint8_t* buf) {
+    const uint8_t* la = buf;
+    const uint8_t* lb = buf + FS::kA;
+    const uint32_t* lsa = reinterpret_cast<const uint32_t*>(buf + FS::kA + FS::kB);
+    const uint32_t* lsb = lsa + kFusedTM;
+    int sas[kMQ], sbs[kNQ];
+#pragma unroll
+    for (int i = 0; i < kMQ; ++i) sas[i] = (int)(lsa[ar + 32 * i] >> (8 * g));
+#pragma unroll
+    for (int q = 0; q < kNQ; ++q) sbs[q] = (int)(lsb[br + 32 * q] >> (8 * g));
+    constexpr int fa = Operand<AE>::kFmt, fb = Operand<BE>::kFmt;
+    auto kstep = [&](auto H) {
+      constexpr int h = decltype(H)::value;
+      v8i af[kMQ], bf[kNQ];
+#pragma unroll
+      for (int i = 0; i < kMQ; ++i) af[i] = read_operand<AE, kFusedTK>(la, ar + 32 * i, h, g);
+#pragma unroll
+      for (int q = 0; q < kNQ; ++q) bf[q] = read_operand<BE, kFusedTK>(lb, br + 32 * q, h, g);
+      constexpr int sel = 2 * h;  // byte 2h of the shifted dword: block 2h + g of the stage
+#pragma unroll
+      for (int i = 0; i < kMQ; ++i)
+#pragma unroll
+        for (int q = 0; q < kNQ; ++q) {
+          if constexpr (Split<AE, BE>::kA) {
+            const v8i ah = e4m3_high(af[i]);
+            acc[i][q] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                ah, bf[q], acc[i][q], fa, fb, sel, sas[i], sel, sbs[q]);
+            acc[i][q] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                af[i] ^ ah, bf[q], acc[i][q], fa, fb, sel, sas[i], sel, sbs[q]);
+          } else if constexpr (Split<AE, BE>::kB) {
+            const v8i bh = e4m3_high(bf[q]);
+            acc[i][q] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                af[i], bh, acc[i][q], fa, fb, sel, sas[i], sel, sbs[q]);
+            acc[i][q] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                af[i], bf[q] ^ bh, acc[i][q], fa, fb, sel, sas[i], sel, sbs[q]);
+          } else {
+            acc[i][q] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                af[i], bf[q], acc[i][q], fa, fb, sel, sas[i], sel, sbs[q]);
+          }
+        }
+    };
+    static_assert(kFusedTK == 128, "two MFMA K steps per stage");
+    kstep(std::integral_constant<int, 0>{});
+    kstep(std::integral_constant<int, 1>{});
+  };
+
+  load(0);
+  store(0, smem0);
+  for (int st = 0; st < stages; ++st) {
+    __syncthreads();  // stage st is in LDS; the other buffer is free
+    if (st + 1 < stages) load(st + 1);
+    if (st & 1)
+      mfma(smem1);
+    else
+      mfma(smem0);
+    if (st + 1 < stages) store(st + 1, (st & 1) ? smem0 : smem1);
+  }
+
+  // Epilogue as in the tiled kernel: lane holds C[8(e/4) + 4g + (e%4)][lr] of
+  // each 32x32 tile.
+#pragma unroll
+  for (int i = 0; i < kMQ; ++i)
+#pragma unroll
+    for (int q = 0; q < kNQ; ++q) {
+      const int64_t col = n0 + wn * 64 + 32 * q + lr;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t row = m0 + wm * 64 + 32 * i + 8 * (e >> 2) + 4 * g + (e & 3);
+        if (row < M && col < N) {
+          float v = acc[i][q][e];
+          if (accumulate) v += c[row * N + col];
+          __builtin_nontemporal_store(v, c + row * N + col);
+        }
+      }
+    }
+}
+
+template <int AE, int BE>
+hipError_t launch_quant_a_typed(const float* a, const uint8_t* b, const uint8_t* sb, float* c,
+                                int64_t M, int64_t N, int64_t K, int accumulate,
+                                hipStream_t stream) {
+  const int64_t tiles_m = (M + kFusedTM - 1) / kFusedTM, tiles_n = (N + kFusedTN - 1) / kFusedTN;
+  if (tiles_m * tiles_n > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((block_matmul_quant_a<AE, BE>), dim3((unsigned)(tiles_m * tiles_n)),
+                     dim3(kFusedThreads), 0, stream, a, b, sb, c, M, N, K, accumulate,
+                     (int)tiles_m, (int)tiles_n);
+  return hipGetLastError();
+}
+
 template <int AE, int BE>
 hipError_t launch_typed(const uint8_t* a, const uint8_t* sa, const uint8_t* b,
                         const uint8_t* sb, float* c, int64_t M, int64_t N, int64_t K,
@@ -816,6 +1078,19 @@ hipError_t launch_typed(const uint8_t* a, const uint8_t* sa, const uint8_t* b,
 }
 
 }  // namespace
+
+hipError_t launch_block_matmul_quant_a(const float* a, int a_elem, const void* b_codes,
+                                       const uint8_t* b_scales, int b_elem, float* c, int64_t M,
+                                       int64_t N, int64_t K, int accumulate, hipStream_t stream) {
+  const uint8_t* b = static_cast<const uint8_t*>(b_codes);
+  if (a_elem == kE2M1 && b_elem == kE2M1)
+    return launch_quant_a_typed<kE2M1, kE2M1>(a, b, b_scales, c, M, N, K, accumulate, stream);
+  if (a_elem == kE2M1 && b_elem == kE4M3)
+    return launch_quant_a_typed<kE2M1, kE4M3>(a, b, b_scales, c, M, N, K, accumulate, stream);
+  if (a_elem == kE4M3 && b_elem == kE2M1)
+    return launch_quant_a_typed<kE4M3, kE2M1>(a, b, b_scales, c, M, N, K, accumulate, stream);
+  return launch_quant_a_typed<kE4M3, kE4M3>(a, b, b_scales, c, M, N, K, accumulate, stream);
+}
 
 hipError_t launch_block_matmul(const void* a_codes, const uint8_t* a_scales, int a_elem,
                                const void* b_codes, const uint8_t* b_scales, int b_elem,

@@ -80,6 +80,22 @@ mx_status_t mx_block_matmul_f32b(const void* a_codes, const uint8_t* a_scales, m
                                                reinterpret_cast<hipStream_t>(stream)));
 }
 
+mx_status_t mx_block_matmul_quantize_a(const float* a, mx_elem_t a_elem, const void* b_codes,
+                                       const uint8_t* b_scales, mx_elem_t b_elem, float* c,
+                                       int64_t M, int64_t N, int64_t K, int32_t block_size,
+                                       int32_t accumulate, mx_stream_t stream) {
+  if (!a || !b_codes || !b_scales || !c) return MX_ERR_NULL;
+  if (!is_elem(a_elem) || !is_elem(b_elem) || block_size != MX_BLOCK_SIZE)
+    return MX_ERR_UNSUPPORTED;
+  if (M < 1 || N < 1 || K < 1 || K % MX_BLOCK_SIZE != 0) return MX_ERR_SHAPE;
+  if (M > INT64_MAX / K || N > INT64_MAX / K || M > INT64_MAX / N) return MX_ERR_SHAPE;
+  if (!aligned16(a) || !aligned16(b_codes) || (reinterpret_cast<uintptr_t>(c) & 3))
+    return MX_ERR_ALIGN;
+  return from_hip(mx::launch_block_matmul_quant_a(a, (int)a_elem, b_codes, b_scales, (int)b_elem,
+                                                  c, M, N, K, accumulate ? 1 : 0,
+                                                  reinterpret_cast<hipStream_t>(stream)));
+}
+
 mx_status_t mx_quantize_axis(const float* x, void* codes, uint8_t* scales, int64_t rows,
                              int64_t cols, int32_t axis, mx_elem_t elem, int32_t block_size,
                              mx_stream_t stream) {
@@ -129,7 +145,7 @@ const char* mx_status_string(mx_status_t status) {
     case MX_ERR_NULL: return "a required pointer is NULL";
     case MX_ERR_SHAPE: return "invalid shape: sizes must be >= 1 and cols/K a multiple of 32";
     case MX_ERR_UNSUPPORTED: return "unsupported element type or block size (E2M1/E4M3, 32)";
-    case MX_ERR_ALIGN: return "buffer below the required alignment (16 bytes; 4 for the f32-B product's B and C)";
+    case MX_ERR_ALIGN: return "buffer below the required alignment (16 bytes; 4 for the f32-B product's B and C and the fused product's C)";
     case MX_ERR_HIP: return "HIP runtime error at kernel launch";
   }
   return "unknown status";

@@ -33,6 +33,12 @@ hipError_t launch_block_matmul(const void* a_codes, const uint8_t* a_scales, int
                                float* c, int64_t M, int64_t N, int64_t K, int accumulate,
                                hipStream_t stream);
 
+// Float32 A [M, K] quantized along K in the matmul's prologue, times block-
+// scaled B^T [N, K] (block_matmul.hip).  a is 16-byte aligned, K % 32 == 0.
+hipError_t launch_block_matmul_quant_a(const float* a, int a_elem, const void* b_codes,
+                                       const uint8_t* b_scales, int b_elem, float* c, int64_t M,
+                                       int64_t N, int64_t K, int accumulate, hipStream_t stream);
+
 // Block-scaled A times float32 B[K, N] (block_matmul_f32b.hip).
 hipError_t launch_block_matmul_f32b(const void* a_codes, const uint8_t* a_scales, int a_elem,
                                     const float* b, float* c, int64_t M, int64_t N, int64_t K,

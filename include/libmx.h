@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define LIBMX_ABI_VERSION 2
+#define LIBMX_ABI_VERSION 3
 #define MX_BLOCK_SIZE 32
 
 /* Same object as HIP's hipStream_t (a pointer to the runtime's stream). */
@@ -152,6 +152,29 @@ mx_status_t mx_block_matmul(const void *a_codes, const uint8_t *a_scales, mx_ele
 mx_status_t mx_block_matmul_f32b(const void *a_codes, const uint8_t *a_scales, mx_elem_t a_elem,
                                  const float *b, float *c, int64_t M, int64_t N, int64_t K,
                                  int32_t block_size, int32_t accumulate, mx_stream_t stream);
+
+/*
+ * mx_block_matmul_quantize_a -- C = [accumulate ? C : 0] + Q(A) . B, with A an
+ * ordinary float32 matrix quantized inside the product.  The dialect page,
+ * section "The four ops": quantize_block is the one lossy step and feeds
+ * block_matmul; here the two run as one kernel, so the quantized A is never
+ * written to memory.  Q is exactly mx_quantize(A, a_elem) (the same scale
+ * bytes and codes, bit for bit), and the product is that of mx_block_matmul
+ * on Q(A) and B^T, with the same accuracy per format pair.
+ *   A:   device float32 [M, K], row-major, 16-byte aligned (read).
+ *   B^T: b_codes [N, K or K/2] (16-byte aligned) + b_scales [N, K/32] (any
+ *        alignment), element type b_elem.
+ *   C:   device float32 [M, N], 4-byte aligned; read only if accumulate != 0.
+ * A block of A holding NaN or Inf gets scale byte 0xFF, so its row of C is
+ * NaN.  Each A row is quantized once per 128-column tile of C (N / 128 times
+ * in all), which is why the separate mx_quantize + mx_block_matmul stays the
+ * faster route for large N.
+ * Errors as mx_block_matmul (MX_ERR_ALIGN for a misaligned a, b_codes or c).
+ */
+mx_status_t mx_block_matmul_quantize_a(const float *a, mx_elem_t a_elem, const void *b_codes,
+                                       const uint8_t *b_scales, mx_elem_t b_elem, float *c,
+                                       int64_t M, int64_t N, int64_t K, int32_t block_size,
+                                       int32_t accumulate, mx_stream_t stream);
 
 /*
  * mx_quantize_axis / mx_dequantize_axis -- the codec with an explicit block

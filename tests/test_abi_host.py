@@ -32,7 +32,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
-        "mx_abi_version", "mx_block_matmul", "mx_block_matmul_f32b", "mx_codes_bytes",
+        "mx_abi_version", "mx_block_matmul", "mx_block_matmul_f32b", "mx_block_matmul_quantize_a",
+        "mx_codes_bytes",
         "mx_dequantize",
         "mx_dequantize_axis", "mx_fold_scale", "mx_num_scale_blocks", "mx_quantize",
         "mx_quantize_axis", "mx_status_string"])
@@ -44,7 +45,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version(L):
-    assert B.mx_abi_version() == 2
+    assert B.mx_abi_version() == 3
 
 
 def test_size_helpers(L):
@@ -139,6 +140,19 @@ def test_matmul_f32b_validation(L, over, status):
                                   a["K"], a["bs"], a["acc"], None) == status
 
 
+@pytest.mark.parametrize("over,status", [
+    (dict(a=0), 1), (dict(b=0), 1), (dict(sb=0), 1), (dict(c=0), 1),
+    (dict(ae=0), 3), (dict(be=5), 3), (dict(bs=64), 3),
+    (dict(M=0), 2), (dict(N=0), 2), (dict(K=0), 2), (dict(K=40), 2), (dict(M=-2), 2),
+    (dict(a=X + 4), 4), (dict(b=C + 8), 4), (dict(c=Y + 2), 4),
+])
+def test_matmul_quantize_a_validation(L, over, status):
+    a = dict(a=X, ae=2, b=C, sb=S, be=1, c=Y, M=16, N=16, K=128, bs=32, acc=0)
+    a.update(over)
+    assert L.mx_block_matmul_quantize_a(a["a"], a["ae"], a["b"], a["sb"], a["be"], a["c"],
+                                        a["M"], a["N"], a["K"], a["bs"], a["acc"], None) == status
+
+
 def test_python_layer_rejects_cpu_tensors(L):
     import torch
     with pytest.raises(ValueError):
@@ -182,6 +196,13 @@ def test_python_layer_checks_buffer_sizes(L):
         B.block_matmul(a, _mx(16, 64, B.MX_E2M1, scales_n=31))
     with pytest.raises(ValueError, match=size):
         B.block_matmul_f32b(a, torch.zeros(64, 5), out=torch.zeros(8, 6))
+    with pytest.raises(ValueError, match=size):                   # fused quantize + matmul
+        B.block_matmul_quantize_a(torch.zeros(8, 64), B.MX_E4M3, bt, out=torch.zeros(8, 17))
+    with pytest.raises(ValueError, match=size):
+        B.block_matmul_quantize_a(torch.zeros(8, 64), B.MX_E4M3, _mx(16, 64, B.MX_E2M1,
+                                                                      codes_n=16 * 31))
+    with pytest.raises(ValueError, match="K mismatch"):
+        B.block_matmul_quantize_a(torch.zeros(8, 96), B.MX_E4M3, bt)
     with pytest.raises(ValueError, match="element type"):
         B.dequantize(B.MXTensor(torch.zeros(4), torch.zeros(4), 1, 32, 7))
 

@@ -37,6 +37,7 @@ def test_graph_replays_match_eager():
         B.block_matmul(o["xa"], o["wq"], out=o["c_tiled"])            # 512 x 512 x 2048
         B.block_matmul(o["x16"], o["wq"], out=o["c_skinny"])          # 16 x 512 x 2048
         B.block_matmul_f32b(o["wq"], bf, out=o["c_f32b"])             # 512 x 48 x 2048
+        B.block_matmul_quantize_a(x, B.MX_E4M3, o["wq"], out=o["c_fused"])  # 512 x 512 x 2048
         B.quantize(w, B.MX_E2M1, out=o["w0"], axis=0)
         B.dequantize(o["w0"], out=o["w0d"])
         B.fold_scale(o["w0"], 3)
@@ -51,6 +52,7 @@ def test_graph_replays_match_eager():
             "c_tiled": torch.empty(512, 512, device="cuda"),
             "c_skinny": torch.empty(16, 512, device="cuda"),
             "c_f32b": torch.empty(512, 48, device="cuda"),
+            "c_fused": torch.empty(512, 512, device="cuda"),
             "w0": B.empty_mx(512, 2048, B.MX_E2M1, x.device, axis=0),
             "w0d": torch.empty(512, 2048, device="cuda"),
         }
