@@ -477,6 +477,23 @@ def bench_matmuls(mx, W, torch, reps, ref=None):
         out["mxfp8_8192x8192x8192"]["sustained_clock_mhz"] = round(mhz)
         out["mxfp8_8192x8192x8192"]["frac_at_sustained_clock"] = round(
             tf / (PEAK_TFLOPS["fp8"] * mhz / 2400.0), 4)
+    # Operands from HBM: back to back, the 138 MB of operands stay in the 256
+    # MiB Infinity Cache; rotating three copies (415 MB) makes every call
+    # fetch them from HBM.
+    ops = [(at, btt)] + [(mx.MXTensor(at.codes.clone(), at.scales.clone(), at.rows, at.cols, at.elem),
+                          mx.MXTensor(btt.codes.clone(), btt.scales.clone(), btt.rows, btt.cols,
+                                      btt.elem)) for _ in range(2)]
+    kk = [0]
+
+    def fp8_cold():
+        kk[0] = (kk[0] + 1) % len(ops)
+        mx.block_matmul(ops[kk[0]][0], ops[kk[0]][1], out=c)
+    cms, cmn = timed(torch, "fp8_cold", fp8_cold, 3 * max(1, reps // 3))
+    out["mxfp8_8192x8192x8192"]["cold_operands"] = {
+        "ms": round(cms, 4), "tflops": round(flops / (cms * 1e-3) / 1e12, 1),
+        "frac": round(flops / (cms * 1e-3) / 1e12 / PEAK_TFLOPS["fp8"], 4),
+        "what": "each call reads one of 3 operand copies (415 MB, beyond the Infinity Cache)"}
+    del ops
     if ref:
         r, k = ref["rows"]["mxfp8"]
         torch.cuda.synchronize()
@@ -498,6 +515,18 @@ def bench_matmuls(mx, W, torch, reps, ref=None):
         mx.block_matmul(aq, btt, out=c)
 
     ms, mn = timed(torch, "prefill", prefill, reps)
+    # Operands from HBM: rotate three copies of the activations and the
+    # weight (3 x 189 MB) so that no call finds them in the Infinity Cache.
+    pops = [(ad, btt)] + [(ad.clone(), mx.MXTensor(btt.codes.clone(), btt.scales.clone(), btt.rows,
+                                                    btt.cols, btt.elem)) for _ in range(2)]
+    pk = [0]
+
+    def prefill_cold():
+        pk[0] = (pk[0] + 1) % len(pops)
+        mx.quantize(pops[pk[0]][0], mx.MX_E4M3, out=aq)
+        mx.block_matmul(aq, pops[pk[0]][1], out=c)
+    pcms, _ = timed(torch, "prefill_cold", prefill_cold, 3 * max(1, reps // 3))
+    del pops
     qms, _ = timed(torch, "prefill_q", lambda: mx.quantize(ad, mx.MX_E4M3, out=aq), reps)
     mms, _ = timed(torch, "prefill_mm", lambda: mx.block_matmul(aq, btt, out=c), reps)
     progress(f"prefill linear done: {ms:.3f} ms")
@@ -507,6 +536,9 @@ def bench_matmuls(mx, W, torch, reps, ref=None):
     out["prefill_e4m3xe2m1_2048x28672x8192"] = {
         "ms": round(ms, 4), "min_ms": round(mn, 4), "tflops": round(tf, 1),
         "quantize_ms": round(qms, 4), "matmul_ms": round(mms, 4),
+        "cold_operands": {"ms": round(pcms, 4), "tflops": round(flops / (pcms * 1e-3) / 1e12, 1),
+                          "what": "each call reads one of 3 copies of activations and weight "
+                                  "(567 MB, beyond the Infinity Cache)"},
         "roofline": {"bound": "mfma", "kernel": "block_matmul", "achieved": round(tfm, 1),
                      "peak": PEAK_TFLOPS["fp8"], "unit": "TFLOP/s",
                      "frac": round(tfm / PEAK_TFLOPS["fp8"], 4)}}
