@@ -807,10 +807,10 @@ hipError_t launch_skinny(const uint8_t* a, const uint8_t* sa, const uint8_t* b,
 // in the layout of the tiled kernel (so its operand reads, the exact split of
 // an E4M3 operand against E2M1, and its epilogue apply unchanged).
 //
-// Tiles of 128 x 128, 4 waves of 64 x 64 (2 x 2 MFMA tiles of 32x32x64).
-// Two LDS stages: stage st + 1's global loads are issued before stage st's
-// MFMAs and quantized after them.  A's rows are read (and quantized) once per
-// tile column, i.e. N / 128 times over: the price of not storing Q(A).
+// Tiles of 128 x 128, 4 waves of 64 x 64 (2 x 2 MFMA tiles of 32x32x64), two
+// LDS stage buffers, two workgroups per CU: one workgroup's loads and encode
+// overlap the other's MFMAs.  A's rows are read (and quantized) once per tile
+// column, i.e. N / 128 times over: the price of not storing Q(A).
 //
 // A loads: wave w covers rows 32w .. 32w + 31 of the tile, two rows per
 // 16-byte load instruction (lane l: row 2i + l / 32, floats 4 (l % 32) .. + 3
@@ -872,18 +872,12 @@ block_matmul_quant_a(const float* __restrict__ a, const uint8_t* __restrict__ b,
   constexpr int kBChunkK = BE == kE2M1 ? 32 : 16;                 // K elements per chunk
 
   const int acol = 4 * (lane & 31);  // this lane's first float of a stage row
-  float4 av[16];
-  uint4 bv[FS::kBPieces];
-  uint32_t bsv = 0x7F7F7F7Fu;
 
-  auto load = [&](int st) {
-    const int64_t k = (int64_t)st * kFusedTK + acol;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int64_t row = min(m0 + 32 * wave + 2 * i + (lane >> 5), M - 1);
-      av[i] = k < K ? *reinterpret_cast<const float4*>(a + row * K + k)
-                    : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+  // B^T's codes of stage st (plain 16-byte loads) and, for t < TN, the scale
+  // dword of row n0 + t (blocks past K and rows past N get scale 2^0: their
+  // codes are zero, and a 0xFF byte would poison the row in the MFMA).
+  auto stage_b = [&](int st, uint8_t* buf) {
+    uint4 bv[FS::kBPieces];
 #pragma unroll
     for (int p = 0; p < FS::kBPieces; ++p) {
       const int P = p * kFusedThreads + t;
@@ -894,70 +888,75 @@ block_matmul_quant_a(const float* __restrict__ a, const uint8_t* __restrict__ b,
                                                    (int64_t)st * kBRowBytes + 16 * ch)
                  : make_uint4(0u, 0u, 0u, 0u);
     }
+    uint32_t bsv = 0;
     if (t < kFusedTN) {
-      // Blocks past K or rows past N get scale 2^0 (their codes are zero; a
-      // 0xFF byte would poison the row in the MFMA).
-      uint32_t w = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int64_t kb = 4 * (int64_t)st + j;
         const uint32_t byte = (n0 + t < N && kb < kblocks) ? sb[(n0 + t) * kblocks + kb] : 127u;
-        w |= byte << (8 * j);
+        bsv |= byte << (8 * j);
       }
-      bsv = w;
     }
+    return [=]() {
+#pragma unroll
+      for (int p = 0; p < FS::kBPieces; ++p) {
+        const int P = p * kFusedThreads + t;
+        *reinterpret_cast<uint4*>(buf + FS::kA +
+                                  lds_off<BE, kFusedTK>(P / FS::kBChunks, P % FS::kBChunks)) = bv[p];
+      }
+      if (t < kFusedTN) reinterpret_cast<uint32_t*>(buf + FS::kA + FS::kB)[kFusedTM + t] = bsv;
+    };
   };
 
-  auto store = [&](int st, uint8_t* buf) {
-    uint8_t* la = buf;
-    uint8_t* lb = buf + FS::kA;
-    uint32_t* lsa = reinterpret_cast<uint32_t*>(buf + FS::kA + FS::kB);
-    uint32_t* lsb = lsa + kFusedTM;
-    const bool k_live = (int64_t)st * kFusedTK + acol < K;
-    uint32_t amax[16], low = 0xFFFFFFFFu;
+  // Quantize A's row pairs 4c .. 4c + 3 of this wave for stage st into buf:
+  // their loads, the block amax over each group of 8 lanes, the encode (the
+  // hardware convert unless a live lane of the wave holds a possible
+  // midpoint; the results are the same either way), codes and scale bytes
+  // into LDS.  Working in chunks of four keeps 16 floats per lane live
+  // instead of 64, which lets two workgroups share a CU.
+  auto quant_chunk = [&](int st, int c, uint8_t* buf) {
+    const int64_t k = (int64_t)st * kFusedTK + acol;
+    float4 v[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t b0 = __float_as_uint(av[i].x), b1 = __float_as_uint(av[i].y);
-      const uint32_t b2 = __float_as_uint(av[i].z), b3 = __float_as_uint(av[i].w);
-      amax[i] = max(max(b0 & 0x7FFFFFFFu, b1 & 0x7FFFFFFFu), max(b2 & 0x7FFFFFFFu, b3 & 0x7FFFFFFFu));
-      const bool live = k_live && m0 + 32 * wave + 2 * i + (lane >> 5) < M;
-      if (live)
+    for (int j = 0; j < 4; ++j) {
+      const int64_t row = min(m0 + 32 * wave + 2 * (4 * c + j) + (lane >> 5), M - 1);
+      v[j] = k < K ? *reinterpret_cast<const float4*>(a + row * K + k)
+                   : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    uint32_t amax[4], low = 0xFFFFFFFFu;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t b0 = __float_as_uint(v[j].x), b1 = __float_as_uint(v[j].y);
+      const uint32_t b2 = __float_as_uint(v[j].z), b3 = __float_as_uint(v[j].w);
+      amax[j] = max(max(b0 & 0x7FFFFFFFu, b1 & 0x7FFFFFFFu), max(b2 & 0x7FFFFFFFu, b3 & 0x7FFFFFFFu));
+      if (k < K && m0 + 32 * wave + 2 * (4 * c + j) + (lane >> 5) < M)
         low = min(low, min(min(b0 << F::kTieShift, b1 << F::kTieShift),
                            min(b2 << F::kTieShift, b3 << F::kTieShift)));
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) amax[i] = max_over_8_lanes(amax[i]);
+    for (int j = 0; j < 4; ++j) amax[j] = max_over_8_lanes(amax[j]);
     bool exact = low == 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) exact |= amax[i] < 0x0D800000u;
+    for (int j = 0; j < 4; ++j) exact |= amax[j] < 0x0D800000u;
     const bool fast = __ballot(exact) == 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = 32 * wave + 2 * i + (lane >> 5);  // row within the tile
-      const uint32_t am = amax[i];
-      const int e = codec::block_exponent<AE>(am);
-      const bool nonfinite = am >= 0x7F800000u;
-      const uint32_t byte = am == 0 ? 127u : (nonfinite ? 0xFFu : (uint32_t)(e + 127));
+    for (int j = 0; j < 4; ++j) {
+      const int r = 32 * wave + 2 * (4 * c + j) + (lane >> 5);  // row within the tile
+      const int e = codec::block_exponent<AE>(amax[j]);
+      const bool nonfinite = amax[j] >= 0x7F800000u;
+      const uint32_t byte = amax[j] == 0 ? 127u : (nonfinite ? 0xFFu : (uint32_t)(e + 127));
       const float scale = __uint_as_float((uint32_t)max(e + 127, 1) << 23);
       const float inv_scale = __uint_as_float((uint32_t)(127 - e) << 23);
-      uint32_t w = fast ? codec::convert4<AE>(av[i], scale, AE == kE4M3 ? 448.0f * scale : 0.0f)
-                        : codec::round4<AE>(av[i], inv_scale);
+      uint32_t w = fast ? codec::convert4<AE>(v[j], scale, AE == kE4M3 ? 448.0f * scale : 0.0f)
+                        : codec::round4<AE>(v[j], inv_scale);
       w = nonfinite ? 0u : w;
       if (AE == kE4M3)
-        *reinterpret_cast<uint32_t*>(la + lds_off<AE, kFusedTK>(r, acol >> 4) + (acol & 15)) = w;
+        *reinterpret_cast<uint32_t*>(buf + lds_off<AE, kFusedTK>(r, acol >> 4) + (acol & 15)) = w;
       else
-        *reinterpret_cast<uint16_t*>(la + lds_off<AE, kFusedTK>(r, acol >> 5) +
+        *reinterpret_cast<uint16_t*>(buf + lds_off<AE, kFusedTK>(r, acol >> 5) +
                                      ((acol >> 1) & 15)) = (uint16_t)w;
       if ((lane & 7) == 0) buf[FS::kA + FS::kB + 4 * r + ((lane & 31) >> 3)] = (uint8_t)byte;
     }
-#pragma unroll
-    for (int p = 0; p < FS::kBPieces; ++p) {
-      const int P = p * kFusedThreads + t;
-      *reinterpret_cast<uint4*>(lb + lds_off<BE, kFusedTK>(P / FS::kBChunks, P % FS::kBChunks)) =
-          bv[p];
-    }
-    if (t < kFusedTN) lsb[t] = bsv;
-    (void)lsa;
   };
 
   v16f acc[kMQ][kNQ];
@@ -1015,16 +1014,16 @@ block_matmul_quant_a(const float* __restrict__ a, const uint8_t* __restrict__ b,
     kstep(std::integral_constant<int, 1>{});
   };
 
-  load(0);
-  store(0, smem0);
+  // One barrier per stage: it follows this stage's LDS writes and every
+  // wave's MFMAs of the previous stage, whose buffer the next stage rewrites.
   for (int st = 0; st < stages; ++st) {
-    __syncthreads();  // stage st is in LDS; the other buffer is free
-    if (st + 1 < stages) load(st + 1);
-    if (st & 1)
-      mfma(smem1);
-    else
-      mfma(smem0);
-    if (st + 1 < stages) store(st + 1, (st & 1) ? smem0 : smem1);
+    uint8_t* buf = (st & 1) ? smem1 : smem0;
+    auto put_b = stage_b(st, buf);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) quant_chunk(st, c, buf);
+    put_b();
+    __syncthreads();
+    mfma(buf);
   }
 
   // Epilogue as in the tiled kernel: lane holds C[8(e/4) + 4g + (e%4)][lr] of
