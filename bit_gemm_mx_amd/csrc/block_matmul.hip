@@ -807,19 +807,22 @@ hipError_t launch_skinny(const uint8_t* a, const uint8_t* sa, const uint8_t* b,
 // in the layout of the tiled kernel (so its operand reads, the exact split of
 // an E4M3 operand against E2M1, and its epilogue apply unchanged).
 //
-// Tiles of 128 x 128, 4 waves of 64 x 64 (2 x 2 MFMA tiles of 32x32x64), two
-// LDS stage buffers, two workgroups per CU: one workgroup's loads and encode
-// overlap the other's MFMAs.  A's rows are read (and quantized) once per tile
-// column, i.e. N / 128 times over: the price of not storing Q(A).
+// Tiles of 128 x 256, 8 waves of 64 x 64 (2 x 2 MFMA tiles of 32x32x64), two
+// LDS stage buffers; a wave's loads and encode overlap the other wave's
+// MFMAs on its SIMD.  A's rows are read (and quantized) once per tile column,
+// i.e. N / 256 times over: the price of not storing Q(A).  (Measured on the
+// prefill workload: 128 x 128 tiles 2.78 ms, 128 x 256 1.91 ms.)
 //
-// A loads: wave w covers rows 32w .. 32w + 31 of the tile, two rows per
+// A loads: wave w covers rows 16w .. 16w + 15 of the tile, two rows per
 // 16-byte load instruction (lane l: row 2i + l / 32, floats 4 (l % 32) .. + 3
 // of the stage), so one instruction reads two contiguous 512-byte row pieces
 // and each aligned group of 8 lanes holds one 32-element block, whose amax is
 // reduced across the 8 lanes as in the quantize kernel.
 // ---------------------------------------------------------------------------
-constexpr int kFusedTM = 128, kFusedTN = 128, kFusedTK = 128;
-constexpr int kFusedThreads = 256;
+constexpr int kFusedTM = 128, kFusedTN = 256, kFusedTK = 128;
+constexpr int kFusedWN = kFusedTN / 64;                   // waves along N; 2 along M
+constexpr int kFusedThreads = 64 * 2 * kFusedWN;
+constexpr int kFusedPairs = kFusedTM / (2 * kFusedWN) / 2;  // A row pairs each wave encodes
 
 // Max of v over each aligned group of 8 lanes.
 __device__ __forceinline__ uint32_t max_over_8_lanes(uint32_t v) {
@@ -864,7 +867,7 @@ block_matmul_quant_a(const float* __restrict__ a, const uint8_t* __restrict__ b,
 
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int wm = wave >> 1, wn = wave & 1, g = lane >> 5, lr = lane & 31;
+  const int wm = wave / kFusedWN, wn = wave % kFusedWN, g = lane >> 5, lr = lane & 31;
   const int64_t kblocks = K / 32;
   const int stages = (int)((K + kFusedTK - 1) / kFusedTK);
   constexpr int kBRowBytes = Stage<BE, kFusedTK>::kRowBytes;      // per stage
@@ -912,14 +915,15 @@ block_matmul_quant_a(const float* __restrict__ a, const uint8_t* __restrict__ b,
   // their loads, the block amax over each group of 8 lanes, the encode (the
   // hardware convert unless a live lane of the wave holds a possible
   // midpoint; the results are the same either way), codes and scale bytes
-  // into LDS.  Working in chunks of four keeps 16 floats per lane live
-  // instead of 64, which lets two workgroups share a CU.
+  // into LDS.  Chunks of four keep 16 floats per lane live (all of a wave's
+  // rows at once measured 4.47 ms against 2.78 ms with 128 x 128 tiles: the
+  // registers cost a wave per SIMD).
   auto quant_chunk = [&](int st, int c, uint8_t* buf) {
     const int64_t k = (int64_t)st * kFusedTK + acol;
     float4 v[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int64_t row = min(m0 + 32 * wave + 2 * (4 * c + j) + (lane >> 5), M - 1);
+      const int64_t row = min(m0 + 2 * kFusedPairs * wave + 2 * (4 * c + j) + (lane >> 5), M - 1);
       v[j] = k < K ? *reinterpret_cast<const float4*>(a + row * K + k)
                    : make_float4(0.f, 0.f, 0.f, 0.f);
     }
@@ -929,7 +933,7 @@ block_matmul_quant_a(const float* __restrict__ a, const uint8_t* __restrict__ b,
       const uint32_t b0 = __float_as_uint(v[j].x), b1 = __float_as_uint(v[j].y);
       const uint32_t b2 = __float_as_uint(v[j].z), b3 = __float_as_uint(v[j].w);
       amax[j] = max(max(b0 & 0x7FFFFFFFu, b1 & 0x7FFFFFFFu), max(b2 & 0x7FFFFFFFu, b3 & 0x7FFFFFFFu));
-      if (k < K && m0 + 32 * wave + 2 * (4 * c + j) + (lane >> 5) < M)
+      if (k < K && m0 + 2 * kFusedPairs * wave + 2 * (4 * c + j) + (lane >> 5) < M)
         low = min(low, min(min(b0 << F::kTieShift, b1 << F::kTieShift),
                            min(b2 << F::kTieShift, b3 << F::kTieShift)));
     }
@@ -941,7 +945,7 @@ block_matmul_quant_a(const float* __restrict__ a, const uint8_t* __restrict__ b,
     const bool fast = __ballot(exact) == 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int r = 32 * wave + 2 * (4 * c + j) + (lane >> 5);  // row within the tile
+      const int r = 2 * kFusedPairs * wave + 2 * (4 * c + j) + (lane >> 5);  // row in the tile
       const int e = codec::block_exponent<AE>(amax[j]);
       const bool nonfinite = amax[j] >= 0x7F800000u;
       const uint32_t byte = amax[j] == 0 ? 127u : (nonfinite ? 0xFFu : (uint32_t)(e + 127));
@@ -1020,7 +1024,7 @@ block_matmul_quant_a(const float* __restrict__ a, const uint8_t* __restrict__ b,
     uint8_t* buf = (st & 1) ? smem1 : smem0;
     auto put_b = stage_b(st, buf);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) quant_chunk(st, c, buf);
+    for (int c = 0; c < kFusedPairs / 4; ++c) quant_chunk(st, c, buf);
     put_b();
     __syncthreads();
     mfma(buf);
