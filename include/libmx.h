@@ -166,7 +166,7 @@ mx_status_t mx_block_matmul_f32b(const void *a_codes, const uint8_t *a_scales, m
  *        alignment), element type b_elem.
  *   C:   device float32 [M, N], 4-byte aligned; read only if accumulate != 0.
  * A block of A holding NaN or Inf gets scale byte 0xFF, so its row of C is
- * NaN.  Each A row is quantized once per 128-column tile of C (N / 128 times
+ * NaN.  Each A row is quantized once per 256-column tile of C (N / 256 times
  * in all), which is why the separate mx_quantize + mx_block_matmul stays the
  * faster route for large N.
  * Errors as mx_block_matmul (MX_ERR_ALIGN for a misaligned a, b_codes or c).
