@@ -811,7 +811,8 @@ hipError_t launch_skinny(const uint8_t* a, const uint8_t* sa, const uint8_t* b,
 // LDS stage buffers; a wave's loads and encode overlap the other wave's
 // MFMAs on its SIMD.  A's rows are read (and quantized) once per tile column,
 // i.e. N / 256 times over: the price of not storing Q(A).  (Measured on the
-// prefill workload: 128 x 128 tiles 2.78 ms, 128 x 256 1.91 ms.)
+// prefill workload: 128 x 128 tiles 2.78 ms, 128 x 256 1.91 ms, and 1.78 ms
+// with the next stage's loads in flight during the MFMAs.)
 //
 // A loads: wave w covers rows 16w .. 16w + 15 of the tile, two rows per
 // 16-byte load instruction (lane l: row 2i + l / 32, floats 4 (l % 32) .. + 3
@@ -876,11 +877,15 @@ block_matmul_quant_a(const float* __restrict__ a, const uint8_t* __restrict__ b,
 
   const int acol = 4 * (lane & 31);  // this lane's first float of a stage row
 
-  // B^T's codes of stage st (plain 16-byte loads) and, for t < TN, the scale
-  // dword of row n0 + t (blocks past K and rows past N get scale 2^0: their
-  // codes are zero, and a 0xFF byte would poison the row in the MFMA).
-  auto stage_b = [&](int st, uint8_t* buf) {
-    uint4 bv[FS::kBPieces];
+  // Registers carrying a stage's global loads: B^T's codes (plain 16-byte
+  // loads), for t < TN the scale dword of row n0 + t, and this wave's A rows.
+  // Stage st + 1's loads are issued right after stage st's barrier, so that
+  // they land while stage st's MFMAs run.
+  uint4 bv[FS::kBPieces];
+  uint32_t bsv = 0;
+  float4 av[kFusedPairs];  // row pair i: row 2i + lane / 32 of this wave's rows
+
+  auto load_stage = [&](int st) {
 #pragma unroll
     for (int p = 0; p < FS::kBPieces; ++p) {
       const int P = p * kFusedThreads + t;
@@ -891,76 +896,81 @@ block_matmul_quant_a(const float* __restrict__ a, const uint8_t* __restrict__ b,
                                                    (int64_t)st * kBRowBytes + 16 * ch)
                  : make_uint4(0u, 0u, 0u, 0u);
     }
-    uint32_t bsv = 0;
     if (t < kFusedTN) {
+      // Blocks past K and rows past N get scale 2^0: their codes are zero, and
+      // a 0xFF byte would poison the row in the MFMA.
+      uint32_t w = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int64_t kb = 4 * (int64_t)st + j;
         const uint32_t byte = (n0 + t < N && kb < kblocks) ? sb[(n0 + t) * kblocks + kb] : 127u;
-        bsv |= byte << (8 * j);
+        w |= byte << (8 * j);
       }
+      bsv = w;
     }
-    return [=]() {
+    const int64_t k = (int64_t)st * kFusedTK + acol;
 #pragma unroll
-      for (int p = 0; p < FS::kBPieces; ++p) {
-        const int P = p * kFusedThreads + t;
-        *reinterpret_cast<uint4*>(buf + FS::kA +
-                                  lds_off<BE, kFusedTK>(P / FS::kBChunks, P % FS::kBChunks)) = bv[p];
-      }
-      if (t < kFusedTN) reinterpret_cast<uint32_t*>(buf + FS::kA + FS::kB)[kFusedTM + t] = bsv;
-    };
+    for (int i = 0; i < kFusedPairs; ++i) {
+      const int64_t row = min(m0 + 2 * kFusedPairs * wave + 2 * i + (lane >> 5), M - 1);
+      av[i] = k < K ? *reinterpret_cast<const float4*>(a + row * K + k)
+                    : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
   };
 
-  // Quantize A's row pairs 4c .. 4c + 3 of this wave for stage st into buf:
-  // their loads, the block amax over each group of 8 lanes, the encode (the
+  // Encode stage st's A rows (already in av) into buf, four row pairs at a
+  // time: the block amax over each group of 8 lanes, the encode (the
   // hardware convert unless a live lane of the wave holds a possible
-  // midpoint; the results are the same either way), codes and scale bytes
-  // into LDS.  Chunks of four keep 16 floats per lane live (all of a wave's
-  // rows at once measured 4.47 ms against 2.78 ms with 128 x 128 tiles: the
-  // registers cost a wave per SIMD).
-  auto quant_chunk = [&](int st, int c, uint8_t* buf) {
+  // midpoint; the results are the same either way), codes and scale bytes;
+  // then B^T's codes and scales.
+  auto store_stage = [&](int st, uint8_t* buf) {
     const int64_t k = (int64_t)st * kFusedTK + acol;
-    float4 v[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t row = min(m0 + 2 * kFusedPairs * wave + 2 * (4 * c + j) + (lane >> 5), M - 1);
-      v[j] = k < K ? *reinterpret_cast<const float4*>(a + row * K + k)
-                   : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int c = 0; c < kFusedPairs / 4; ++c) {
+      uint32_t amax[4], low = 0xFFFFFFFFu;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 v = av[4 * c + j];
+        const uint32_t b0 = __float_as_uint(v.x), b1 = __float_as_uint(v.y);
+        const uint32_t b2 = __float_as_uint(v.z), b3 = __float_as_uint(v.w);
+        amax[j] = max(max(b0 & 0x7FFFFFFFu, b1 & 0x7FFFFFFFu),
+                      max(b2 & 0x7FFFFFFFu, b3 & 0x7FFFFFFFu));
+        if (k < K && m0 + 2 * kFusedPairs * wave + 2 * (4 * c + j) + (lane >> 5) < M)
+          low = min(low, min(min(b0 << F::kTieShift, b1 << F::kTieShift),
+                             min(b2 << F::kTieShift, b3 << F::kTieShift)));
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) amax[j] = max_over_8_lanes(amax[j]);
+      bool exact = low == 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) exact |= amax[j] < 0x0D800000u;
+      const bool fast = __ballot(exact) == 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 2 * kFusedPairs * wave + 2 * (4 * c + j) + (lane >> 5);  // row in the tile
+        const int e = codec::block_exponent<AE>(amax[j]);
+        const bool nonfinite = amax[j] >= 0x7F800000u;
+        const uint32_t byte = amax[j] == 0 ? 127u : (nonfinite ? 0xFFu : (uint32_t)(e + 127));
+        const float scale = __uint_as_float((uint32_t)max(e + 127, 1) << 23);
+        const float inv_scale = __uint_as_float((uint32_t)(127 - e) << 23);
+        const float4 v = av[4 * c + j];
+        uint32_t w = fast ? codec::convert4<AE>(v, scale, AE == kE4M3 ? 448.0f * scale : 0.0f)
+                          : codec::round4<AE>(v, inv_scale);
+        w = nonfinite ? 0u : w;
+        if (AE == kE4M3)
+          *reinterpret_cast<uint32_t*>(buf + lds_off<AE, kFusedTK>(r, acol >> 4) + (acol & 15)) = w;
+        else
+          *reinterpret_cast<uint16_t*>(buf + lds_off<AE, kFusedTK>(r, acol >> 5) +
+                                       ((acol >> 1) & 15)) = (uint16_t)w;
+        if ((lane & 7) == 0) buf[FS::kA + FS::kB + 4 * r + ((lane & 31) >> 3)] = (uint8_t)byte;
+      }
     }
-    uint32_t amax[4], low = 0xFFFFFFFFu;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t b0 = __float_as_uint(v[j].x), b1 = __float_as_uint(v[j].y);
-      const uint32_t b2 = __float_as_uint(v[j].z), b3 = __float_as_uint(v[j].w);
-      amax[j] = max(max(b0 & 0x7FFFFFFFu, b1 & 0x7FFFFFFFu), max(b2 & 0x7FFFFFFFu, b3 & 0x7FFFFFFFu));
-      if (k < K && m0 + 2 * kFusedPairs * wave + 2 * (4 * c + j) + (lane >> 5) < M)
-        low = min(low, min(min(b0 << F::kTieShift, b1 << F::kTieShift),
-                           min(b2 << F::kTieShift, b3 << F::kTieShift)));
+    for (int p = 0; p < FS::kBPieces; ++p) {
+      const int P = p * kFusedThreads + t;
+      *reinterpret_cast<uint4*>(buf + FS::kA +
+                                lds_off<BE, kFusedTK>(P / FS::kBChunks, P % FS::kBChunks)) = bv[p];
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) amax[j] = max_over_8_lanes(amax[j]);
-    bool exact = low == 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) exact |= amax[j] < 0x0D800000u;
-    const bool fast = __ballot(exact) == 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = 2 * kFusedPairs * wave + 2 * (4 * c + j) + (lane >> 5);  // row in the tile
-      const int e = codec::block_exponent<AE>(amax[j]);
-      const bool nonfinite = amax[j] >= 0x7F800000u;
-      const uint32_t byte = amax[j] == 0 ? 127u : (nonfinite ? 0xFFu : (uint32_t)(e + 127));
-      const float scale = __uint_as_float((uint32_t)max(e + 127, 1) << 23);
-      const float inv_scale = __uint_as_float((uint32_t)(127 - e) << 23);
-      uint32_t w = fast ? codec::convert4<AE>(v[j], scale, AE == kE4M3 ? 448.0f * scale : 0.0f)
-                        : codec::round4<AE>(v[j], inv_scale);
-      w = nonfinite ? 0u : w;
-      if (AE == kE4M3)
-        *reinterpret_cast<uint32_t*>(buf + lds_off<AE, kFusedTK>(r, acol >> 4) + (acol & 15)) = w;
-      else
-        *reinterpret_cast<uint16_t*>(buf + lds_off<AE, kFusedTK>(r, acol >> 5) +
-                                     ((acol >> 1) & 15)) = (uint16_t)w;
-      if ((lane & 7) == 0) buf[FS::kA + FS::kB + 4 * r + ((lane & 31) >> 3)] = (uint8_t)byte;
-    }
+    if (t < kFusedTN) reinterpret_cast<uint32_t*>(buf + FS::kA + FS::kB)[kFusedTM + t] = bsv;
   };
 
   v16f acc[kMQ][kNQ];
@@ -1020,13 +1030,12 @@ block_matmul_quant_a(const float* __restrict__ a, const uint8_t* __restrict__ b,
 
   // One barrier per stage: it follows this stage's LDS writes and every
   // wave's MFMAs of the previous stage, whose buffer the next stage rewrites.
+  load_stage(0);
   for (int st = 0; st < stages; ++st) {
     uint8_t* buf = (st & 1) ? smem1 : smem0;
-    auto put_b = stage_b(st, buf);
-#pragma unroll
-    for (int c = 0; c < kFusedPairs / 4; ++c) quant_chunk(st, c, buf);
-    put_b();
+    store_stage(st, buf);
     __syncthreads();
+    if (st + 1 < stages) load_stage(st + 1);
     mfma(buf);
   }
 
