@@ -808,8 +808,8 @@ hipError_t launch_skinny(const uint8_t* a, const uint8_t* sa, const uint8_t* b,
 // an E4M3 operand against E2M1, and its epilogue apply unchanged).
 //
 // Tiles of 128 x 256, 8 waves of 64 x 64 (2 x 2 MFMA tiles of 32x32x64), two
-// LDS stage buffers; a wave's loads and encode overlap the other wave's
-// MFMAs on its SIMD.  A's rows are read (and quantized) once per tile column,
+// LDS stage buffers; stage st + 1's global loads go out after stage st's
+// barrier and land during its MFMAs.  A's rows are read (and quantized) once per tile column,
 // i.e. N / 256 times over: the price of not storing Q(A).  (Measured on the
 // prefill workload: 128 x 128 tiles 2.78 ms, 128 x 256 1.91 ms, and 1.78 ms
 // with the next stage's loads in flight during the MFMAs.)
