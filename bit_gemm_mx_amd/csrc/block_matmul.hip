@@ -401,6 +401,7 @@ __device__ __forceinline__ v8i read_operand(const uint8_t* lds, int r, int h, in
 // s_waitcnt immediate (gfx9 encoding) that waits until at most n vector
 // memory operations are outstanding, leaving the other counters alone.
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+constexpr int kLgkmZero = 0xC07F;  // s_waitcnt lgkmcnt(0), other counters untouched
 
 // Scale staging.  Chunk mode (K a multiple of 512): one 16-byte slice per row
 // (16 blocks = 512 K) per chunk of stages, in two chunk buffers by parity.
@@ -772,6 +773,204 @@ hipError_t launch_tiled_split(const uint8_t* a, const uint8_t* sa, const uint8_t
                                                             accumulate, stream);
 }
 
+// ---------------------------------------------------------------------------
+// Staged skinny kernel, for up to 32 rows of A (token-by-token decode) with K
+// a multiple of 128.  The work split is the skinny kernel's (8 waves per 16
+// columns of C, a contiguous range of K steps per wave, the 8 partial tiles
+// summed in LDS in wave order), but the operands reach the MFMAs through LDS
+// instead of register permutes:
+//   * each wave stages a batch of U K steps of its 16 B^T rows and 16 T A
+//     rows, and their scale dwords, with buffer loads that write LDS directly.
+//     One 16-byte load instruction fills 1 KiB, 16 consecutive lanes reading
+//     256 contiguous bytes of one row, so a batch touches the fewest cache
+//     lines a row-major read can;
+//   * after its own loads have landed (vmcnt; the region is the wave's own,
+//     so no barrier), the wave reads each 32-element block of an MFMA
+//     operand with one 16-byte LDS read, where the register path needs four
+//     dword permutes for the same 16 bytes;
+//   * 16-byte chunk c of row r of a staged span sits at chunk position
+//     c ^ (r % 16) of that row (128-byte spans pair rows into 256-byte
+//     lines), so the 16 lanes that read one block of 16 rows address 16
+//     different bank groups;
+//   * rows past the matrix read as zeros (the buffer range), their outputs
+//     are not stored; K steps past the wave's range are loaded but not
+//     multiplied.
+// ---------------------------------------------------------------------------
+template <int AE, int BE, int T>
+struct StagedSkinny {
+  static constexpr int kStepA = AE == kE2M1 ? 64 : 128;  // bytes per row and 128-K step
+  static constexpr int kStepB = BE == kE2M1 ? 64 : 128;
+  // Per wave: B^T codes, A codes, then 16-byte scale rows of B^T and A.
+  static constexpr int wave_bytes(int u) {
+    return 16 * u * (T * kStepA + kStepB) + 256 * (1 + T);
+  }
+  static constexpr int kRed = kSkinnyWaves * T * 64 * 16;
+  static constexpr int kU = kSkinnyWaves * wave_bytes(4) + kRed <= 160 * 1024 ? 4 : 2;
+  static constexpr int kSpanA = kU * kStepA, kSpanB = kU * kStepB;  // 128 .. 512 bytes
+  static constexpr int kCodesA = 16 * T * kSpanA, kCodesB = 16 * kSpanB;
+  static constexpr int kWaveBytes = wave_bytes(kU);
+  static_assert(kCodesA % 1024 == 0 && kCodesB % 1024 == 0, "whole 1-KiB load instructions");
+};
+
+// LDS offset of 16-byte chunk c of row r in a staged span of SPAN bytes per row.
+template <int SPAN>
+__device__ __forceinline__ int span_off(int r, int c) {
+  if constexpr (SPAN >= 256) {
+    return r * SPAN + ((c ^ (r & 15)) << 4);
+  } else {
+    static_assert(SPAN == 128, "spans of 128, 256 or 512 bytes");
+    return (r >> 1) * 256 + (((((r & 1) << 3) | c) ^ ((r >> 1) & 7)) << 4);
+  }
+}
+
+// Stage ROWS rows x SPAN bytes (from byte byte0 of each row) at `lds`: the
+// lane that writes LDS offset o fetches the chunk span_off maps to o.
+template <int SPAN, int ROWS, int AUX>
+__device__ __forceinline__ void stage_span(uint8_t* lds, __amdgpu_buffer_rsrc_t rsrc,
+                                           uint32_t row_bytes, uint32_t byte0, int lane) {
+#pragma unroll
+  for (int j = 0; j < ROWS * SPAN / 1024; ++j) {
+    const int o = 1024 * j + 16 * lane;
+    int r, c;
+    if constexpr (SPAN >= 256) {
+      r = o / SPAN;
+      c = ((o % SPAN) >> 4) ^ (r & 15);
+    } else {
+      const int line = o >> 8, q = ((o & 255) >> 4) ^ (line & 7);
+      r = 2 * line + (q >> 3);
+      c = q & 7;
+    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc, (__attribute__((address_space(3))) void*)(lds + 1024 * j), 16,
+        (uint32_t)r * row_bytes + byte0 + 16u * c, 0, 0, AUX);
+  }
+}
+
+// MFMA operand (row r, K step u, lane group g) from a staged span.
+template <int ELEM, int SPAN>
+__device__ __forceinline__ v8i read_span(const uint8_t* lds, int r, int u, int g) {
+  if constexpr (ELEM == kE4M3) {
+    const v4i lo = *reinterpret_cast<const v4i*>(lds + span_off<SPAN>(r, 8 * u + g));
+    const v4i hi = *reinterpret_cast<const v4i*>(lds + span_off<SPAN>(r, 8 * u + 4 + g));
+    return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  } else {
+    const v4i lo = *reinterpret_cast<const v4i*>(lds + span_off<SPAN>(r, 4 * u + g));
+    return v8i{lo.x, lo.y, lo.z, lo.w, 0, 0, 0, 0};
+  }
+}
+
+template <int AE, int BE, int T>
+__global__ void __launch_bounds__(kSkinnyThreads)
+block_matmul_skinny_staged(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa,
+                           const uint8_t* __restrict__ b, const uint8_t* __restrict__ sb,
+                           float* __restrict__ c, int64_t M, int64_t N, int64_t K,
+                           int accumulate) {
+  using S = StagedSkinny<AE, BE, T>;
+  constexpr int U = S::kU;
+  __shared__ __align__(1024) uint8_t lds[kSkinnyWaves * S::kWaveBytes];
+  __shared__ v4f red[kSkinnyWaves][T][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, g = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int64_t kblocks = K / 32, steps = K / 128;
+  const int64_t per_wave = (steps + kSkinnyWaves - 1) / kSkinnyWaves;
+  const int64_t s_begin = wave * per_wave;
+  const int64_t s_end = min(steps, s_begin + per_wave);
+  const uint32_t rb_a = (uint32_t)(K / 128 * S::kStepA), rb_b = (uint32_t)(K / 128 * S::kStepB);
+  const int64_t rows_b = min((int64_t)16, N - n0), rows_a = min((int64_t)(16 * T), M);
+  const __amdgpu_buffer_rsrc_t code_b = make_rsrc(b + n0 * rb_b, rows_b * rb_b);
+  const __amdgpu_buffer_rsrc_t code_a = make_rsrc(a, rows_a * rb_a);
+  const __amdgpu_buffer_rsrc_t scale_b = make_rsrc(sb + n0 * kblocks, rows_b * kblocks);
+  const __amdgpu_buffer_rsrc_t scale_a = make_rsrc(sa, rows_a * kblocks);
+  uint8_t* const lds_b = lds + wave * S::kWaveBytes;
+  uint8_t* const lds_a = lds_b + S::kCodesB;
+  uint8_t* const lds_sb = lds_a + S::kCodesA;
+  uint8_t* const lds_sa = lds_sb + 256;
+  // Scale load lane l: row l / 4 (of each 16-row group), step l % 4 of the batch.
+  const int srow = lane >> 2, sstep = lane & 3;
+
+  v4f acc[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int64_t s0 = s_begin; s0 < s_end; s0 += U) {
+    const int n_steps = (int)min((int64_t)U, s_end - s0);  // wave-uniform
+    stage_span<S::kSpanB, 16, 2>(lds_b, code_b, rb_b, (uint32_t)(s0 * S::kStepB), lane);
+    stage_span<S::kSpanA, 16 * T, 0>(lds_a, code_a, rb_a, (uint32_t)(s0 * S::kStepA), lane);
+    const uint32_t soff = (uint32_t)(4 * (s0 + sstep));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        scale_b, (__attribute__((address_space(3))) void*)lds_sb, 4,
+        sstep < U ? (uint32_t)(srow * kblocks) + soff : kOutOfRange, 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          scale_a, (__attribute__((address_space(3))) void*)(lds_sa + 256 * t), 4,
+          sstep < U ? (uint32_t)((16 * t + srow) * kblocks) + soff : kOutOfRange, 0, 0, 0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    // All of the batch's LDS reads first (one round trip), then the MFMAs.
+    // A step past the wave's range multiplies zero codes by zero codes at
+    // scale 1 (its staged bytes belong to other steps or rows, NaN codes
+    // included), adding +0 to accumulators that never hold -0, so the MFMA
+    // sequence has no branch for the reads to sink behind.
+    const v4i bsd = *reinterpret_cast<const v4i*>(lds_sb + 16 * r16);
+    v4i asd[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+      asd[t] = *reinterpret_cast<const v4i*>(lds_sa + 16 * (16 * t + r16));
+    v8i bm[U], am[U][T];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      bm[u] = read_span<BE, S::kSpanB>(lds_b, r16, u, g);
+#pragma unroll
+      for (int t = 0; t < T; ++t) am[u][t] = read_span<AE, S::kSpanA>(lds_a, 16 * t + r16, u, g);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool live = u < n_steps;
+      const int bs = live ? bsd[u] >> (8 * g) : 127;
+      const v8i b_op = live ? bm[u] : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+      const v8i bh = Split<AE, BE>::kB ? e4m3_high(b_op) : b_op;
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const int as = live ? asd[t][u] >> (8 * g) : 127;
+        const v8i a_op = live ? am[u][t] : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+        if constexpr (Split<AE, BE>::kA) {
+          const v8i ah = e4m3_high(a_op);
+          acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              ah, b_op, acc[t], Operand<AE>::kFmt, Operand<BE>::kFmt, 0, as, 0, bs);
+          acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              a_op ^ ah, b_op, acc[t], Operand<AE>::kFmt, Operand<BE>::kFmt, 0, as, 0, bs);
+        } else if constexpr (Split<AE, BE>::kB) {
+          acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              a_op, bh, acc[t], Operand<AE>::kFmt, Operand<BE>::kFmt, 0, as, 0, bs);
+          acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              a_op, b_op ^ bh, acc[t], Operand<AE>::kFmt, Operand<BE>::kFmt, 0, as, 0, bs);
+        } else {
+          acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              a_op, b_op, acc[t], Operand<AE>::kFmt, Operand<BE>::kFmt, 0, as, 0, bs);
+        }
+      }
+    }
+    // The next batch's loads overwrite this wave's LDS region: its reads are done.
+    __builtin_amdgcn_s_waitcnt(kLgkmZero);
+  }
+#pragma unroll
+  for (int t = 0; t < T; ++t) red[wave][t][lane] = acc[t];
+  __syncthreads();
+  for (int o = threadIdx.x; o < T * 256; o += kSkinnyThreads) {
+    const int t = o >> 8, rr = (o >> 4) & 15, cc = o & 15;
+    const int src = 16 * (rr >> 2) + cc, j = rr & 3;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kSkinnyWaves; ++w) v += red[w][t][src][j];
+    const int64_t row = 16 * t + rr, col = n0 + cc;
+    if (row < M && col < N) {
+      if (accumulate) v += c[row * N + col];
+      c[row * N + col] = v;
+    }
+  }
+}
+
 template <int AE, int BE>
 hipError_t launch_skinny(const uint8_t* a, const uint8_t* sa, const uint8_t* b,
                          const uint8_t* sb, float* c, int64_t M, int64_t N, int64_t K,
@@ -785,6 +984,16 @@ hipError_t launch_skinny(const uint8_t* a, const uint8_t* sa, const uint8_t* b,
   // starts on a dword boundary and holds whole steps.
   const int dw = (K % 128 == 0) && ((reinterpret_cast<uintptr_t>(sa) & 3) == 0) &&
                  ((reinterpret_cast<uintptr_t>(sb) & 3) == 0);
+  // The staged kernel addresses 32 rows of an operand with 32-bit buffer offsets.
+  if (dw && t <= 2 && 32 * K < (1ll << 31)) {
+    if (t == 1)
+      hipLaunchKernelGGL((block_matmul_skinny_staged<AE, BE, 1>), dim3((unsigned)gx),
+                         dim3(kSkinnyThreads), 0, stream, a, sa, b, sb, c, M, N, K, accumulate);
+    else
+      hipLaunchKernelGGL((block_matmul_skinny_staged<AE, BE, 2>), dim3((unsigned)gx),
+                         dim3(kSkinnyThreads), 0, stream, a, sa, b, sb, c, M, N, K, accumulate);
+    return hipGetLastError();
+  }
   if (t == 1)
     hipLaunchKernelGGL((block_matmul_skinny<AE, BE, 1>), grid, dim3(kSkinnyThreads), 0, stream,
                        a, sa, b, sb, c, M, N, K, accumulate, dw);

@@ -47,9 +47,12 @@ def rand_operand(rng, rows, K, elem, lo=112, hi=142, nan_codes=False):
 # the waves of a workgroup in one or many load batches, K not a multiple of
 # 128, several row panels), shapes the 256x256-tile kernel does not take
 # (K not a multiple of 128), and shapes it does take with partial tiles in M
-# and N.
+# and N.  Up to 32 rows with K a multiple of 128 run the LDS-staged decode
+# kernel: one K step in all (a partial batch), ranges of 2 and 1 steps with
+# idle waves (K = 1152), two row tiles, ragged N.
 SHAPES = [(1, 1, 32), (3, 4, 96), (16, 16, 128), (17, 33, 160), (64, 48, 1024),
-          (33, 100, 4128), (5, 70, 8192), (2, 17, 65536), (200, 70, 1056),
+          (33, 100, 4128), (5, 70, 8192), (2, 17, 65536), (32, 50, 1152), (24, 16, 384),
+          (20, 300, 4224), (12, 1000, 2048), (200, 70, 1056),
           (100, 70, 3968), (256, 256, 512), (300, 257, 2080), (257, 300, 1152),
           (130, 520, 640), (512, 256, 128),
           # the tiled kernel (M > 64, K a multiple of 512) with partial tiles in M and N
@@ -99,11 +102,12 @@ def test_random_codes(ae, be, M, N, K):
     assert_matmul_close(got, want, mag)
 
 
+@pytest.mark.parametrize("M", [140, 24])
 @pytest.mark.parametrize("ae,be", PAIRS)
-def test_accumulate(ae, be):
-    rng = np.random.default_rng(77)
+def test_accumulate(ae, be, M):
+    rng = np.random.default_rng(77 + M)
     fp8 = ae == be == O.E4M3
-    M, N, K = (140, 72, 2048) if fp8 else (140, 72, 384)
+    N, K = (72, 2048) if fp8 else (72, 384)
     ac, asc = quantized_normal(rng, M, K, ae, outliers=0.0 if fp8 else 0.01)
     bc, bsc = quantized_normal(rng, N, K, be, outliers=0.0 if fp8 else 0.01)
     cin = (rng.standard_normal((M, N)) * 1e7).astype(np.float32)
@@ -123,11 +127,15 @@ def test_accumulate_zero_overwrites_without_reading():
     assert_matmul_close(got, want, mag)
 
 
+@pytest.mark.parametrize("M", [33, 30])
 @pytest.mark.parametrize("ae,be", PAIRS)
-def test_nan_scales_and_codes(ae, be):
-    """0xFF scales and E4M3 NaN codes poison exactly the oracle's outputs."""
+def test_nan_scales_and_codes(ae, be, M):
+    """0xFF scales and E4M3 NaN codes poison exactly the oracle's outputs.
+    M = 30 runs the LDS-staged decode kernel, whose waves here stage a batch
+    of K steps and multiply only the first: the unused steps staged for B^T
+    row 29 hold row 30's NaN code, which must not reach column 29."""
     rng = np.random.default_rng(79)
-    M, N, K = 33, 35, 256
+    N, K = 35, 256
     fp8 = ae == be == O.E4M3
     if fp8:      # Gaussian data: the single-instruction pair's T1 regime
         ac, asc = quantized_normal(rng, M, K, ae, outliers=0.0)
