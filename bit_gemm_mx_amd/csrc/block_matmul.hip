@@ -779,11 +779,12 @@ hipError_t launch_tiled_split(const uint8_t* a, const uint8_t* sa, const uint8_t
 // columns of C, a contiguous range of K steps per wave, the 8 partial tiles
 // summed in LDS in wave order), but the operands reach the MFMAs through LDS
 // instead of register permutes:
-//   * each wave stages a batch of U K steps of its 16 B^T rows and 16 T A
-//     rows, and their scale dwords, with buffer loads that write LDS directly.
-//     One 16-byte load instruction fills 1 KiB, 16 consecutive lanes reading
-//     256 contiguous bytes of one row, so a batch touches the fewest cache
-//     lines a row-major read can;
+//   * each wave stages a batch of U K steps (4, or 2 where two row tiles of
+//     E4M3 codes would not fit the LDS) of its 16 B^T rows and 16 T A rows,
+//     and their scale dwords, with buffer loads that write LDS directly.  One
+//     16-byte load instruction fills 1 KiB, consecutive lanes reading a row's
+//     whole span (128 to 512 contiguous bytes), so a batch touches the fewest
+//     cache lines a row-major read can;
 //   * after its own loads have landed (vmcnt; the region is the wave's own,
 //     so no barrier), the wave reads each 32-element block of an MFMA
 //     operand with one 16-byte LDS read, where the register path needs four
@@ -793,8 +794,8 @@ hipError_t launch_tiled_split(const uint8_t* a, const uint8_t* sa, const uint8_t
 //     lines), so the 16 lanes that read one block of 16 rows address 16
 //     different bank groups;
 //   * rows past the matrix read as zeros (the buffer range), their outputs
-//     are not stored; K steps past the wave's range are loaded but not
-//     multiplied.
+//     are not stored; K steps of a batch past the wave's range are multiplied
+//     as zero codes (see the MFMA loop).
 // ---------------------------------------------------------------------------
 template <int AE, int BE, int T>
 struct StagedSkinny {
