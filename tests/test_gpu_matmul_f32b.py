@@ -5,7 +5,9 @@ Bound, per output element: |gpu - oracle| <= 1e-5 * sum_k |a_k b_k|
 (+ |C_in| when accumulating), the matmul tolerance of the quantized path,
 with identical NaN positions and exact zeros where the bound is 0.  Shapes
 cover every launch shape (16x16 tiles with K split over the waves, operands
-loaded element-wise or streamed through LDS; 128x64 tiles), ragged M, N and
+loaded element-wise or streamed through LDS; 128x64 tiles on the float32
+matrix cores, and on the bf16 ones with B split into exact parts, including
+the values that split cannot carry), ragged M, N and
 K, a B that is not 16-byte aligned, and the two measured workloads in full: decode
 (MXFP4 weights 4096x4096 times float32 activations 4096x16) and the square
 4096^3 product.
@@ -49,6 +51,11 @@ def run(ac, asc, elem, b, M, N, K, c_in=None, accumulate=False):
 SHAPES = [(1, 1, 32), (3, 5, 64), (16, 16, 128), (17, 33, 160), (70, 100, 1056), (5, 7, 8192),
           (300, 520, 2048), (1024, 1024, 512), (1030, 1100, 320), (64, 2048, 96),
           (2100, 1100, 320), (2048, 2048, 1024)]
+# Shapes for the 128x64-tile launch on the bf16 matrix cores (at least 256
+# tiles, K % 128 == 0, N % 4 == 0): N ragged within a 64-column tile (a
+# wave's columns past N read the next B row), M ragged, one group of four
+# blocks (K = 128) so the load ring runs past K, K not a multiple of 512.
+BF16_SHAPES = [(2048, 1028, 384), (2000, 2048, 640), (4096, 1024, 128), (1100, 2052, 256)]
 # Shapes for the streamed K-split launch (K % 256 == 0, N % 4 == 0, few tiles):
 # one 256-K unit (15 of 16 waves idle), units not a multiple of 16, ragged M,
 # N = 4 and column tiles cut short of 16, the decode shape's K at small M.
@@ -57,7 +64,7 @@ STREAM_SHAPES = [(1, 4, 256), (17, 20, 256), (33, 4, 4352), (100, 36, 8448), (5,
 
 
 @pytest.mark.parametrize("elem", ELEMS)
-@pytest.mark.parametrize("M,N,K", SHAPES + STREAM_SHAPES)
+@pytest.mark.parametrize("M,N,K", SHAPES + STREAM_SHAPES + BF16_SHAPES)
 def test_random_operands(elem, M, N, K):
     rng = np.random.default_rng(M * 131 + N * 7 + K + elem)
     ac, asc = rand_a(rng, M, K, elem)
@@ -82,7 +89,8 @@ def test_quantized_float_weights(elem):
 
 
 @pytest.mark.parametrize("elem", ELEMS)
-@pytest.mark.parametrize("M,N,K", [(20, 30, 96), (1100, 300, 256), (40, 20, 1024)])
+@pytest.mark.parametrize("M,N,K", [(20, 30, 96), (1100, 300, 256), (40, 20, 1024),
+                                   (2048, 1024, 256)])
 def test_accumulate(elem, M, N, K):
     rng = np.random.default_rng(M + N + K)
     ac, asc = rand_a(rng, M, K, elem)
@@ -119,6 +127,35 @@ def test_nan_scales_codes_and_b(elem):
     assert_matmul_close(got, want, mag)
 
 
+@pytest.mark.parametrize("elem", ELEMS)
+def test_square_shape_values_outside_the_bf16_split(elem):
+    """The 128x64-tile launch multiplies on the bf16 matrix cores, B split
+    into three exact bf16 parts; a block holding a value that split cannot
+    carry exactly runs the float32 MFMAs.  Planted: A scale bytes 0, 1, 2
+    (E4M3 codes there decode below the bf16 subnormals) and a NaN scale; B
+    values whose last bits fall below the bf16 subnormals (a normal value
+    near 2^-120 and a float32 subnormal), +Inf, -Inf and a NaN.  Every output
+    against the oracle: infinities equal, NaN positions equal, the rest
+    within the tolerance."""
+    rng = np.random.default_rng(21 + elem)
+    M, N, K = 2048, 1024, 512
+    ac, asc = rand_a(rng, M, K, elem)
+    asc[5, 3], asc[77, 0], asc[1500, 15] = 0, 1, 2      # rows of three different waves
+    asc[900, 7] = 0xFF
+    b = rand_b(rng, K, N)
+    b[100, 3] = np.float32(1.2345 * 2.0 ** -120)
+    b[200, 500] = np.float32(3e-41)
+    b[300, 700] = np.inf
+    b[301, 701] = -np.inf
+    b[400, 900] = np.nan
+    got = run(ac, asc, elem, b, M, N, K)
+    want, mag = O.block_matmul_f32b(ac, asc, elem, b, M, N, K)
+    inf = np.isinf(want)
+    assert inf.sum() > 100 and np.isnan(want[900]).all() and np.isnan(want[:, 900]).all()
+    np.testing.assert_array_equal(got[inf], want[inf])
+    assert_matmul_close(np.where(inf, 0, got), np.where(inf, 0, want), np.where(inf, 0, mag))
+
+
 def test_zero_rows_and_identity():
     rng = np.random.default_rng(6)
     M, K = 48, 64
@@ -144,13 +181,16 @@ def exhaustive_a(elem, M, K):
 
 
 @pytest.mark.parametrize("elem", ELEMS)
-@pytest.mark.parametrize("M,K", [(256, 256), (2048, 1024)])
+@pytest.mark.parametrize("M,K", [(256, 256), (2048, 1024), (2048, 1056)])
 def test_identity_b_decodes_every_code_and_scale_exactly(elem, M, K):
     """C = A . I is A's exact decode (each output is one product with 1 plus
     zeros), so this pins the in-register decode -- the hardware's scaled
-    converts -- value for value, for every finite code at every scale byte
-    that keeps it finite, subnormal results included.  256 rows take the
-    K-split launch shape, 2048 x 1024 the 128x64-tile shape."""
+    converts to float32, and to bf16 on the bf16 matrix cores -- value for
+    value, for every finite code at every scale byte that keeps it finite,
+    subnormal results included.  256 rows take the K-split launch shape,
+    2048 x 1024 the 128x64-tile shape on the bf16 matrix cores (E4M3 rows at
+    scale bytes 0..2 on the float32 ones), 2048 x 1056 (K not a multiple of
+    128) the 128x64-tile shape on the float32 matrix cores."""
     ac, asc = exhaustive_a(elem, M, K)
     got = run(ac, asc, elem, np.eye(K, dtype=np.float32), M, K, K)
     want = O.dequantize(ac, asc, elem, K)
