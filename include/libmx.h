@@ -147,7 +147,7 @@ mx_status_t mx_block_matmul(const void *a_codes, const uint8_t *a_scales, mx_ele
  *   C[m,n] = sum_j 2^(sa[m,j]-127) * sum_{k in block j} qa[m,k] * B[k,n]
  * in float32 precision: each product is rounded to float32 or (on the bf16
  * matrix cores, with B split into three exact bf16 parts) exact, partial
- * sums span at most a few blocks before they are added in float32, and every
+ * sums span at most 16 blocks before they are added in float32, and every
  * output lies within 1e-5 * sum_k |a_k b_k| of the exact value; a NaN scale
  * or E4M3 NaN code in row m of A makes row m of C NaN.
  * Errors as mx_block_matmul (MX_ERR_ALIGN for a misaligned a_codes, b or c).
