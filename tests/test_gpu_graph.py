@@ -27,6 +27,8 @@ def test_graph_replays_match_eager():
     x = torch.from_numpy(W.normal_with_outliers(rng, (512, 2048), 1.0, 0.01, 30.0)).cuda()
     w = torch.from_numpy(W.normal_with_outliers(rng, (512, 2048), 0.02, 0.001, 50.0)).cuda()
     bf = torch.from_numpy(rng.standard_normal((2048, 48), dtype=np.float32)).cuda()
+    xs = torch.from_numpy(W.normal_with_outliers(rng, (2048, 256), 0.02, 0.001, 50.0)).cuda()
+    bsq = torch.from_numpy(rng.standard_normal((256, 1024), dtype=np.float32)).cuda()
     x16 = x[:16].contiguous()
 
     def run(o):
@@ -37,6 +39,8 @@ def test_graph_replays_match_eager():
         B.block_matmul(o["xa"], o["wq"], out=o["c_tiled"])            # 512 x 512 x 2048
         B.block_matmul(o["x16"], o["wq"], out=o["c_skinny"])          # 16 x 512 x 2048
         B.block_matmul_f32b(o["wq"], bf, out=o["c_f32b"])             # 512 x 48 x 2048
+        B.quantize(xs, B.MX_E2M1, out=o["xs"])
+        B.block_matmul_f32b(o["xs"], bsq, out=o["c_f32b_sq"])         # 2048 x 1024 x 256 (bf16 cores)
         B.block_matmul_quantize_a(x, B.MX_E4M3, o["wq"], out=o["c_fused"])  # 512 x 512 x 2048
         B.quantize(w, B.MX_E2M1, out=o["w0"], axis=0)
         B.dequantize(o["w0"], out=o["w0d"])
@@ -52,6 +56,8 @@ def test_graph_replays_match_eager():
             "c_tiled": torch.empty(512, 512, device="cuda"),
             "c_skinny": torch.empty(16, 512, device="cuda"),
             "c_f32b": torch.empty(512, 48, device="cuda"),
+            "xs": B.empty_mx(2048, 256, B.MX_E2M1, x.device),
+            "c_f32b_sq": torch.empty(2048, 1024, device="cuda"),
             "c_fused": torch.empty(512, 512, device="cuda"),
             "w0": B.empty_mx(512, 2048, B.MX_E2M1, x.device, axis=0),
             "w0d": torch.empty(512, 2048, device="cuda"),
