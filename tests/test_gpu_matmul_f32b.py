@@ -156,6 +156,30 @@ def test_square_shape_values_outside_the_bf16_split(elem):
     assert_matmul_close(np.where(inf, 0, got), np.where(inf, 0, want), np.where(inf, 0, mag))
 
 
+@pytest.mark.parametrize("elem", ELEMS)
+def test_square_shape_one_signed_operands(elem):
+    """Positive A and B: every product has the same sign, so the matrix
+    cores' truncation of each partial sum below its largest term (2^-24) does
+    not cancel across products or K steps.  The bf16 launch keeps a tile's sum
+    in the MFMA accumulator for four blocks (twelve MFMAs) before adding it in
+    float32; K = 8192 gives 64 such groups per output.  Every output within
+    the tolerance, and the worst one well inside it."""
+    rng = np.random.default_rng(31 + elem)
+    M, N, K = 2048, 1024, 8192
+    if elem == O.E2M1:
+        el = rng.integers(1, 8, (M, K), dtype=np.uint8)                 # positive codes
+        ac = O.pack_nibbles(el)
+    else:
+        ac = rng.integers(1, 0x7F, (M, K), dtype=np.uint8)              # positive, no NaN
+    asc = rng.integers(110, 145, (M, K // 32), dtype=np.uint8)
+    b = np.abs(rand_b(rng, K, N))
+    got = run(ac, asc, elem, b, M, N, K)
+    want, mag = O.block_matmul_f32b(ac, asc, elem, b, M, N, K)
+    worst = assert_matmul_close(got, want, mag)
+    print(f"one-signed operands, elem {elem}: worst error {worst:.3g} of the tolerance")
+    assert worst < 0.5, f"worst error {worst:.3g} of the tolerance"
+
+
 def test_zero_rows_and_identity():
     rng = np.random.default_rng(6)
     M, K = 48, 64
