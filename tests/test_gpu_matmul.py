@@ -102,6 +102,31 @@ def test_random_codes(ae, be, M, N, K):
     assert_matmul_close(got, want, mag)
 
 
+@pytest.mark.parametrize("ae,be", EXACT_GROUP_PAIRS)
+@pytest.mark.parametrize("M,N,K", [(512, 512, 8192), (16, 512, 8192), (300, 257, 16384)])
+def test_one_signed_operands(ae, be, M, N, K):
+    """Positive codes in A and B^T: every product has the same sign, so no
+    rounding of the float32 accumulation over K cancels another (K = 8192
+    and 16384: 128 and 256 MFMA steps into one accumulator in the tiled
+    kernel, 8 K ranges summed in LDS in the decode kernel).  Every output
+    within the tolerance; the worst is printed (measured: tiled kernel up to
+    0.4 of it at K = 8192 and 0.6 at K = 16384, decode kernel 0.05)."""
+    rng = np.random.default_rng(M + N + K + 3 * ae + be)
+
+    def positive(rows, elem):
+        if elem == O.E2M1:
+            codes = O.pack_nibbles(rng.integers(1, 8, (rows, K), dtype=np.uint8))
+        else:
+            codes = rng.integers(1, 0x7F, (rows, K), dtype=np.uint8)
+        return codes, rng.integers(120, 135, (rows, K // 32), dtype=np.uint8)
+    ac, asc = positive(M, ae)
+    bc, bsc = positive(N, be)
+    got = gpu_matmul(ac, asc, ae, bc, bsc, be, M, N, K)
+    want, mag = O.block_matmul(ac, asc, ae, bc, bsc, be, M, N, K)
+    worst = assert_matmul_close(got, want, mag)
+    print(f"one-signed {ae}x{be} {M}x{N}x{K}: worst error {worst:.3g} of the tolerance")
+
+
 @pytest.mark.parametrize("M", [140, 24])
 @pytest.mark.parametrize("ae,be", PAIRS)
 def test_accumulate(ae, be, M):
