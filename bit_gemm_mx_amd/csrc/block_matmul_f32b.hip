@@ -521,7 +521,21 @@ block_matmul_f32b_bf16(const uint8_t* __restrict__ a, const uint8_t* __restrict_
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, q = lane >> 4;
   const int wm = w >> 1, wn = w & 1;
-  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+  // Tile order: each XCD (workgroups are dealt to the 8 XCDs in turn) takes
+  // a contiguous range of tiles, walked in groups of 4 tile-rows, so that
+  // the tiles running together on one XCD share B's columns and A's rows in
+  // its L2 (measured 0.59 against 0.63 ms on the 4096^3 product; groups of
+  // 2, 8, 16 and 32 rows 0.60-0.62).
+  const int tiles_m = gridDim.x / tiles_n;
+  const int nwg = tiles_m * tiles_n;
+  int pid = blockIdx.x;
+  if ((nwg & 7) == 0) pid = (pid & 7) * (nwg >> 3) + (pid >> 3);
+  constexpr int kGroup = 4;
+  const int in_group = kGroup * tiles_n;
+  const int first_m = (pid / in_group) * kGroup;
+  const int gsize = min(tiles_m - first_m, kGroup);
+  const int tm = first_m + (pid % in_group) % gsize;
+  const int tn = (pid % in_group) / gsize;
   const int64_t m0 = (int64_t)tm * (2 * S::kRows) + wm * S::kRows, n0 = (int64_t)tn * 64 + wn * 32;
   const int64_t kb = K / 32;
   const uint32_t row_bytes = (uint32_t)(kb * kCodeBytes);
