@@ -10,8 +10,9 @@
 // which is the B^T operand layout of mx_block_matmul.  Element encode and
 // decode are those of the last-axis kernels (codec_common.h).
 //
-// Work mapping: lane l of a wave owns column c0 + l and the wave walks kRun
-// consecutive block-rows.  A row segment of 64 columns is 256 contiguous
+// Work mapping: lane l of a wave owns column c0 + l and the wave walks
+// consecutive block-rows (kRun in the per-lane kernels, two per strip in the
+// band kernel).  A row segment of 64 columns is 256 contiguous
 // bytes, so every load (quantize) and store (dequantize) instruction on the
 // float32 side is coalesced, and each lane holds its whole block in 32
 // registers: amax, exponent and rounding need no cross-lane traffic.  Per
@@ -71,6 +72,53 @@ struct Run {
   uint32_t bytes[kRun];    // the run's scale bytes
 };
 
+// Encode one block held in this lane's registers: its codes (16 or 32
+// bytes, element 0 first) and its scale byte.  `live` is false for lanes
+// past the last column, which must not force the wave onto the exact path.
+template <int ELEM>
+__device__ __forceinline__ void encode_block(const float (&v)[32], bool live,
+                                             u4v (&codes)[ELEM == kE2M1 ? 1 : 2],
+                                             uint32_t& byte) {
+  using F = Fmt<ELEM>;
+  uint32_t amax = 0, low = 0xFFFFFFFFu;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const uint32_t b = __float_as_uint(v[j]);
+    amax = max(amax, b & 0x7FFFFFFFu);
+    low = min(low, b << F::kTieShift);
+  }
+  const int e = block_exponent<ELEM>(amax);
+  const bool nonfinite = amax >= 0x7F800000u;
+  byte = amax == 0 ? 127u : (nonfinite ? 0xFFu : (uint32_t)(e + 127));
+  const float inv_scale = __uint_as_float((uint32_t)(127 - e) << 23);
+  const float scale = __uint_as_float((uint32_t)max(e + 127, 1) << 23);
+  const bool exact = live && (low == 0 || amax < 0x0D800000u);
+  uint32_t w[8];  // codes of 4 consecutive elements each
+  if (__ballot(exact) == 0) {
+    const float top = ELEM == kE4M3 ? 448.0f * scale : 0.0f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      w[q] = convert4<ELEM>(make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]),
+                            scale, top);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      w[q] = round4<ELEM>(make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]),
+                          inv_scale);
+  }
+  if (nonfinite) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) w[q] = 0;
+  }
+  if constexpr (ELEM == kE2M1) {
+    codes[0] = u4v{w[0] | (w[1] << 16), w[2] | (w[3] << 16), w[4] | (w[5] << 16),
+                   w[6] | (w[7] << 16)};
+  } else {
+    codes[0] = u4v{w[0], w[1], w[2], w[3]};
+    codes[1] = u4v{w[4], w[5], w[6], w[7]};
+  }
+}
+
 // Encode the run of block-rows [k.i0, k.i0 + run) of this lane's column.
 // Block-rows are loaded kPf ahead of the one being encoded, into a ring of
 // kPf + 1 register buffers indexed at compile time (measured: one block
@@ -78,7 +126,6 @@ struct Run {
 template <int ELEM>
 __device__ __forceinline__ void encode_run(Run<ELEM>& out, const float* __restrict__ x,
                                            int64_t cols, const Task& k, int run) {
-  using F = Fmt<ELEM>;
   constexpr int kPf = 2;
   float vb[kPf + 1][32];
 #pragma unroll
@@ -89,44 +136,7 @@ __device__ __forceinline__ void encode_run(Run<ELEM>& out, const float* __restri
     out.bytes[r] = 127u;
     if (r >= run) break;  // wave-uniform
     if (r + kPf < run) load_block(vb[(r + kPf) % (kPf + 1)], x, k.i0 + r + kPf, cols, k);
-    const float* v = vb[r % (kPf + 1)];
-    uint32_t amax = 0, low = 0xFFFFFFFFu;
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const uint32_t b = __float_as_uint(v[j]);
-      amax = max(amax, b & 0x7FFFFFFFu);
-      low = min(low, b << F::kTieShift);
-    }
-    const int e = block_exponent<ELEM>(amax);
-    const bool nonfinite = amax >= 0x7F800000u;
-    out.bytes[r] = amax == 0 ? 127u : (nonfinite ? 0xFFu : (uint32_t)(e + 127));
-    const float inv_scale = __uint_as_float((uint32_t)(127 - e) << 23);
-    const float scale = __uint_as_float((uint32_t)max(e + 127, 1) << 23);
-    const bool exact = k.live && (low == 0 || amax < 0x0D800000u);
-    uint32_t w[8];  // codes of 4 consecutive elements each
-    if (__ballot(exact) == 0) {
-      const float top = ELEM == kE4M3 ? 448.0f * scale : 0.0f;
-#pragma unroll
-      for (int q = 0; q < 8; ++q)
-        w[q] = convert4<ELEM>(make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]),
-                              scale, top);
-    } else {
-#pragma unroll
-      for (int q = 0; q < 8; ++q)
-        w[q] = round4<ELEM>(make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]),
-                            inv_scale);
-    }
-    if (nonfinite) {
-#pragma unroll
-      for (int q = 0; q < 8; ++q) w[q] = 0;
-    }
-    if (ELEM == kE2M1) {
-      out.codes[r][0] = u4v{w[0] | (w[1] << 16), w[2] | (w[3] << 16), w[4] | (w[5] << 16),
-                            w[6] | (w[7] << 16)};
-    } else {
-      out.codes[r][0] = u4v{w[0], w[1], w[2], w[3]};
-      out.codes[r][Run<ELEM>::kVecs - 1] = u4v{w[4], w[5], w[6], w[7]};
-    }
+    encode_block<ELEM>(vb[r % (kPf + 1)], k.live, out.codes[r], out.bytes[r]);
   }
 }
 
@@ -163,65 +173,100 @@ quantize_axis0_kernel(const float* __restrict__ x, uint8_t* __restrict__ codes,
         o.bytes[0] | (o.bytes[1] << 8) | (o.bytes[2] << 16) | (o.bytes[3] << 24);
 }
 
-// The eight waves of a workgroup take eight consecutive runs (32 block-rows)
-// of the same 64-column strip, then store through LDS: each column's codes
-// for the 32 block-rows are 512 (E2M1) or 1024 (E4M3) contiguous bytes and
-// its 32 scale bytes are contiguous too, so every store instruction writes
-// whole cache lines of a few columns instead of a 64-byte piece (and a
-// 4-byte scale piece) of 64 columns 4 KiB apart.  With the stores removed
-// the 8192x8192 E2M1 quantize reads its input in 46 us; the per-lane
-// stores cost 16 us more, these 11 (four waves per workgroup and 256-byte
-// pieces: 14; sixteen waves and 1 KiB pieces: 10).  Workgroups walk all
-// strips of a row range before the next (bands of 4..32 strips down all
-// rows measured 68-73 us).  Needs rows % 1024 == 0 and 16-byte aligned
-// scale rows.
-constexpr int kGroupRuns = 8;  // runs per workgroup
-constexpr int kStagedThreads = 64 * kGroupRuns;
+// Band kernel.  A workgroup of 16 waves owns a band of 32 block-rows (1024
+// rows) and, within it, kStrips consecutive 64-column strips, which it
+// encodes one after the other: for each strip, wave w encodes block-rows 2w
+// and 2w+1 of the band (lane l = column l of the strip) into LDS, and after
+// a barrier the workgroup stores the strip -- each column's codes for the
+// band (512 or 1024 contiguous bytes) and its 32 scale bytes, whole cache
+// lines per store instruction.  The next strip's first block is loaded
+// before that barrier, so its reads are in flight while the stores drain,
+// and the two LDS buffers alternate by strip (a strip's encode never
+// overwrites what the previous strip's stores still read: every thread
+// passes the next barrier only after its own stores).  Tasks (band, strip)
+// are numbered band-major and workgroup b takes tasks kStrips*b .. +kStrips-1,
+// so the workgroups in flight write whole columns of codes and read every
+// fourth 256-byte piece of all rows.  8192x8192 E2M1 on one box: 53.2 us
+// against 57.0 us for eight waves of four block-rows on one strip per
+// workgroup (the quantize with its stores removed reads its input in
+// 40.8 us; the stores, written contiguously instead of block-major, would
+// take 53.9 us in that kernel -- it is the write stream mixed into the reads
+// that costs, more than its layout).  Needs rows % 1024 == 0 and 16-byte
+// aligned scale rows.
+constexpr int kBandWaves = 16;
+constexpr int kBandRun = 2;  // block-rows per wave and strip
+constexpr int kBandBlocks = kBandWaves * kBandRun;
+constexpr int kBandRows = 32 * kBandBlocks;
+constexpr int kBandThreads = 64 * kBandWaves;
+constexpr int kStrips = 4;   // strips per workgroup
 
 template <int ELEM>
-__global__ void __launch_bounds__(kStagedThreads)
-quantize_axis0_staged_kernel(const float* __restrict__ x, uint8_t* __restrict__ codes,
-                             uint8_t* __restrict__ scales, int64_t rows, int64_t cols) {
+__global__ void __launch_bounds__(kBandThreads)
+quantize_axis0_band_kernel(const float* __restrict__ x, uint8_t* __restrict__ codes,
+                           uint8_t* __restrict__ scales, int64_t rows, int64_t cols) {
   constexpr int kBlockBytes = Run<ELEM>::kBlockBytes, kVecs = Run<ELEM>::kVecs;
-  constexpr int kColBytes = kGroupRuns * kRun * kBlockBytes;  // one column's codes here
-  constexpr int kStride = kColBytes + 16;                     // padded LDS row
-  __shared__ __attribute__((aligned(16))) uint8_t lds_codes[64 * kStride];
-  __shared__ __attribute__((aligned(16))) uint32_t lds_scales[64 * kGroupRuns];
+  constexpr int kColBytes = kBandBlocks * kBlockBytes;  // one column's codes for the band
+  constexpr int kStride = kColBytes + 16;               // padded LDS row
+  __shared__ __attribute__((aligned(16))) uint8_t lds_codes[2][64 * kStride];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_sc[2][64 * kBandBlocks];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t n_strips = (cols + 63) / 64;
-  const int64_t strip = blockIdx.x % n_strips, group = blockIdx.x / n_strips;
-  Task k;
-  k.c = strip * 64 + lane;
-  k.live = k.c < cols;
-  k.ca = k.live ? k.c : cols - 1;
-  k.i0 = (group * kGroupRuns + wave) * kRun;
-  Run<ELEM> o;
-  encode_run<ELEM>(o, x, cols, k, kRun);
-#pragma unroll
-  for (int r = 0; r < kRun; ++r)
-#pragma unroll
-    for (int h = 0; h < kVecs; ++h)
-      *reinterpret_cast<u4v*>(lds_codes + lane * kStride + (wave * kRun + r) * kBlockBytes +
-                              16 * h) = o.codes[r][h];
-  lds_scales[lane * kGroupRuns + wave] =
-      o.bytes[0] | (o.bytes[1] << 8) | (o.bytes[2] << 16) | (o.bytes[3] << 24);
-  __syncthreads();
+  const int64_t first = (int64_t)blockIdx.x * kStrips;
+  // tasks of this workgroup (>= 1: the grid covers the tasks exactly)
+  const int n_tasks = (int)min((int64_t)kStrips, (rows / kBandRows) * n_strips - first);
   const int64_t row_bytes = ELEM == kE2M1 ? rows / 2 : rows;
-  const int64_t c0 = strip * 64, b0 = group * kGroupRuns * kRun;  // first column, block-row
-  constexpr int kChunks = kColBytes / 16;                         // 16-byte chunks per column
-  constexpr int kColsPerPass = kStagedThreads / kChunks;
+  // Block j of this wave's sequence: task first + j / kBandRun, block-row
+  // kBandRun * wave + j % kBandRun of the task's band.  Lanes past the last
+  // column load the last column (and discard it).
+  auto load = [&](float (&v)[32], int j) {
+    const int64_t task = first + j / kBandRun;
+    const int64_t strip = task % n_strips, band = task / n_strips;
+    const int64_t c = min(strip * 64 + lane, cols - 1);
+    const int64_t i = band * kBandBlocks + kBandRun * wave + j % kBandRun;
+    const float* p = x + 32 * i * cols + c;
 #pragma unroll
-  for (int p = 0; p < 64 / kColsPerPass; ++p) {
-    const int col = p * kColsPerPass + threadIdx.x / kChunks, ch = threadIdx.x % kChunks;
-    if (c0 + col < cols)
-      *reinterpret_cast<u4v*>(codes + (c0 + col) * row_bytes + b0 * kBlockBytes + 16 * ch) =
-          *reinterpret_cast<const u4v*>(lds_codes + col * kStride + 16 * ch);
+    for (int q = 0; q < 32; ++q) v[q] = __builtin_nontemporal_load(p + q * cols);
+  };
+  float vb[2][32];
+  load(vb[0], 0);
+#pragma unroll
+  for (int t = 0; t < kStrips; ++t) {
+    if (t >= n_tasks) break;  // workgroup-uniform
+    const int64_t task = first + t;
+    const int64_t strip = task % n_strips, band = task / n_strips;
+    const int64_t c0 = strip * 64;
+    uint8_t* lc = lds_codes[t & 1];
+    uint8_t* ls = lds_sc[t & 1];
+#pragma unroll
+    for (int r = 0; r < kBandRun; ++r) {
+      const int j = t * kBandRun + r;
+      if (j + 1 < n_tasks * kBandRun) load(vb[(j + 1) & 1], j + 1);
+      u4v cv[kVecs];
+      uint32_t byte;
+      encode_block<ELEM>(vb[j & 1], c0 + lane < cols, cv, byte);
+#pragma unroll
+      for (int h = 0; h < kVecs; ++h)
+        *reinterpret_cast<u4v*>(lc + lane * kStride + (kBandRun * wave + r) * kBlockBytes +
+                                16 * h) = cv[h];
+      ls[lane * kBandBlocks + kBandRun * wave + r] = (uint8_t)byte;
+    }
+    __syncthreads();
+    const int64_t b0 = band * kBandBlocks;                 // first block-row of the band
+    constexpr int kChunks = kColBytes / 16;                // 16-byte chunks per column
+    constexpr int kColsPerPass = kBandThreads / kChunks;
+#pragma unroll
+    for (int p = 0; p < 64 / kColsPerPass; ++p) {
+      const int col = p * kColsPerPass + threadIdx.x / kChunks, ch = threadIdx.x % kChunks;
+      if (c0 + col < cols)
+        *reinterpret_cast<u4v*>(codes + (c0 + col) * row_bytes + b0 * kBlockBytes + 16 * ch) =
+            *reinterpret_cast<const u4v*>(lc + col * kStride + 16 * ch);
+    }
+    // 32 scale bytes per column: two 16-byte stores
+    const int sc = threadIdx.x / 2, half = threadIdx.x & 1;
+    if (threadIdx.x < 128 && c0 + sc < cols)
+      *reinterpret_cast<u4v*>(scales + (c0 + sc) * (rows / 32) + b0 + 16 * half) =
+          *reinterpret_cast<const u4v*>(ls + sc * kBandBlocks + 16 * half);
   }
-  // 32 scale bytes per column: two 16-byte stores
-  const int sc = threadIdx.x / 2, half = threadIdx.x & 1;
-  if (threadIdx.x < 128 && c0 + sc < cols)
-    *reinterpret_cast<u4v*>(scales + (c0 + sc) * (rows / 32) + b0 + 16 * half) =
-        *reinterpret_cast<const u4v*>(lds_scales + sc * kGroupRuns + 4 * half);
 }
 
 template <int ELEM>
@@ -306,16 +351,17 @@ Launch plan(const uint8_t* scales, int64_t rows, int64_t cols) {
 hipError_t launch_quantize_axis0(const float* x, void* codes, uint8_t* scales, int64_t rows,
                                  int64_t cols, int elem, hipStream_t stream) {
   uint8_t* c = static_cast<uint8_t*>(codes);
-  if (rows % (32 * kRun * kGroupRuns) == 0 && (reinterpret_cast<uintptr_t>(scales) & 15) == 0) {
-    const int64_t groups = rows / (32 * kRun * kGroupRuns), strips = (cols + 63) / 64;
-    if (groups * strips > 0x7FFFFFFF) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)(groups * strips));
+  if (rows % kBandRows == 0 && (reinterpret_cast<uintptr_t>(scales) & 15) == 0) {
+    const int64_t tasks = (rows / kBandRows) * ((cols + 63) / 64);
+    const int64_t groups = (tasks + kStrips - 1) / kStrips;
+    if (groups > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)groups);
     if (elem == kE2M1)
-      hipLaunchKernelGGL(quantize_axis0_staged_kernel<kE2M1>, grid, dim3(kStagedThreads), 0,
-                         stream, x, c, scales, rows, cols);
+      hipLaunchKernelGGL(quantize_axis0_band_kernel<kE2M1>, grid, dim3(kBandThreads), 0, stream,
+                         x, c, scales, rows, cols);
     else
-      hipLaunchKernelGGL(quantize_axis0_staged_kernel<kE4M3>, grid, dim3(kStagedThreads), 0,
-                         stream, x, c, scales, rows, cols);
+      hipLaunchKernelGGL(quantize_axis0_band_kernel<kE4M3>, grid, dim3(kBandThreads), 0, stream,
+                         x, c, scales, rows, cols);
     return hipGetLastError();
   }
   const Launch l = plan(scales, rows, cols);
