@@ -9,7 +9,8 @@ HBM traffic of the step (2 x 4.53125 B/element) divided by the step time, in
 GB/s.  Inputs are resident in HBM before the timed region; consecutive steps
 rotate over four copies of the workload (4 x 256 MiB of f32, larger than the
 256 MiB Infinity Cache) so that no step reads what the previous one left in
-the caches.
+the caches.  After the W warm-up steps, untimed steps run for 0.5 s more so
+that the K timed steps see the card's steady clocks.
 
 The other workloads are timed in the same run and reported under "parts",
 each with its roofline: the decode-shaped MXFP4 x MXFP4 16x4096x4096 block
@@ -143,9 +144,21 @@ def bench_codec(mx, W, torch, steps, warmup, ref=None):
             timer.run("quantize", lambda: mx.quantize(xs[j], mx.MX_E2M1, out=qs[j]))
             timer.run("dequantize", lambda: mx.dequantize(qs[j], out=ys[j]))
 
+    # W untimed warm-up steps, then more untimed steps until 0.5 s have passed:
+    # from idle the card needs tens of milliseconds to settle its clocks (the
+    # quantize measured 50.2 us per call within the first ~2 ms of work and
+    # 48.3 us at steady state), and the steady state is what a continuously
+    # loaded GPU sees.  The matmul parts warm up the same way (timed()).
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
+    t_warm = time.perf_counter()
+    i = warmup
+    while time.perf_counter() - t_warm < 0.5:
+        for _ in range(50):
+            step(i)
+            i += 1
+        torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         step(i)
