@@ -231,6 +231,34 @@ def test_ragged_sizes_and_guard_bytes(elem, rows, cols):
     assert_bits_equal(y[:rows * cols], O.dequantize(oc, os_, elem, cols).reshape(-1), "dequant")
 
 
+@pytest.mark.parametrize("elem", ELEMS)
+@pytest.mark.parametrize("offset", [1, 3, 8])
+def test_unaligned_scales_and_guard_bytes(elem, offset):
+    """Scale array starting 1, 3 or 8 bytes past a 16-byte boundary: the
+    quantize stores scale bytes one by one (no 16-byte pieces); the bytes
+    around the array stay untouched."""
+    rows, cols = 37, 4160  # 4810 blocks: whole wave iterations and a ragged tail
+    rng = np.random.default_rng(offset * 31 + elem)
+    x = (rng.standard_normal((rows, cols)) * np.exp(rng.uniform(-6, 6, (rows, 1)))).astype(np.float32)
+    oc, os_ = O.quantize(x, elem)
+    nbytes = B.mx_codes_bytes(rows, cols, elem)
+    nsc = B.mx_num_scale_blocks(rows, cols)
+    guard = 4096
+    cbuf = torch.full((nbytes + guard,), 0xAB, dtype=torch.uint8, device="cuda")
+    sbuf = torch.full((guard + nsc + guard,), 0xCD, dtype=torch.uint8, device="cuda")
+    B.mx_quantize(dev(x).data_ptr(), cbuf.data_ptr(), sbuf.data_ptr() + guard + offset, rows, cols,
+                  elem)
+    c, s = host(cbuf), host(sbuf)
+    assert np.all(c[nbytes:] == 0xAB)
+    assert np.all(s[:guard + offset] == 0xCD) and np.all(s[guard + offset + nsc:] == 0xCD)
+    assert_bits_equal(c[:nbytes], oc.reshape(-1), "codes")
+    assert_bits_equal(s[guard + offset:guard + offset + nsc], os_.reshape(-1), "scales")
+    y = torch.empty(rows * cols, dtype=torch.float32, device="cuda")
+    B.mx_dequantize(cbuf.data_ptr(), sbuf.data_ptr() + guard + offset, y.data_ptr(), rows, cols,
+                    elem)
+    assert_bits_equal(host(y), O.dequantize(oc, os_, elem, cols).reshape(-1), "dequant")
+
+
 def test_weight_codec_full_size():
     """8192x8192 N(0, 0.02) with 0.1% outliers x50, quantized in one launch as
     the benchmark does: every code and scale, and every dequantized value,
