@@ -326,6 +326,69 @@ dequantize_axis0_kernel(const uint8_t* __restrict__ codes, const uint8_t* __rest
   }
 }
 
+// Tile kernel for the dequantize.  A workgroup of 4 waves owns 4 adjacent
+// 64-column strips (256 columns) and a run of 4 block-rows; for each
+// block-row every wave decodes its strip's 32 x 64 values (lane = column)
+// into LDS, and after a barrier the workgroup stores the 32 rows as 1 KiB
+// pieces, 16 bytes per lane, where the per-lane kernel stores 256-byte row
+// pieces 4 bytes per lane (32 store instructions per block instead of 8).
+// 8192x8192 E2M1: 47.3 -> 45.5 us (2 or 4 strips per workgroup, one or two
+// LDS tiles, the same; 8 or 16 strips 60-62 us, the LDS then holding one
+// workgroup per CU).  Needs cols % 256 == 0, rows % 128 == 0 and 4-byte
+// aligned scale rows.
+constexpr int kTileStrips = 4;
+constexpr int kTileRun = 4;  // block-rows per workgroup
+
+template <int ELEM>
+__global__ void __launch_bounds__(64 * kTileStrips)
+dequantize_axis0_tile_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                             float* __restrict__ y, int64_t rows, int64_t cols) {
+  typedef float f4v __attribute__((ext_vector_type(4)));
+  constexpr int kBlockBytes = ELEM == kE2M1 ? 16 : 32, kVecs = kBlockBytes / 16;
+  constexpr int kPad = 4;  // floats of padding per LDS row
+  __shared__ __attribute__((aligned(16))) float tile[kTileStrips][32][64 + kPad];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t nbr = rows / 32, groups = cols / (64 * kTileStrips);
+  const int64_t sg = blockIdx.x % groups, i0 = (blockIdx.x / groups) * kTileRun;
+  const int64_t c = (sg * kTileStrips + wave) * 64 + lane;  // this lane's column
+  const int64_t row_bytes = ELEM == kE2M1 ? rows / 2 : rows;
+  const uint32_t sv = *reinterpret_cast<const uint32_t*>(scales + c * nbr + i0);
+  u4v cb[kTileRun][kVecs];
+#pragma unroll
+  for (int r = 0; r < kTileRun; ++r)
+#pragma unroll
+    for (int h = 0; h < kVecs; ++h)
+      cb[r][h] = *reinterpret_cast<const u4v*>(codes + c * row_bytes + (i0 + r) * kBlockBytes +
+                                               16 * h);
+#pragma unroll
+  for (int r = 0; r < kTileRun; ++r) {
+    const uint32_t byte = (sv >> (8 * r)) & 0xFFu;
+    const float s = scale_value(byte);
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      uint32_t o;
+      if (ELEM == kE2M1) {
+        o = decode_e2m1(cb[r][0][j >> 3] >> (4 * (j & 7)), s);
+      } else {
+        const uint32_t word = j < 16 ? cb[r][0][j >> 2] : cb[r][kVecs - 1][(j - 16) >> 2];
+        o = decode_e4m3((word >> (8 * (j & 3))) & 0xFFu, s);
+      }
+      tile[wave][j][lane] = __uint_as_float(byte == 0xFFu ? kNaN : o);
+    }
+    __syncthreads();
+    // 32 rows x 1 KiB: wave w stores rows w, w + 4, ...; lane l the 16 bytes
+    // at columns 4l .. 4l+3 of the workgroup's 256 (strip l / 16).
+    float* yrow = y + 32 * (i0 + r) * cols + sg * 64 * kTileStrips + 4 * lane;
+#pragma unroll
+    for (int p = 0; p < 32 / kTileStrips; ++p) {
+      const int row = kTileStrips * p + wave;
+      const f4v v = *reinterpret_cast<const f4v*>(&tile[lane >> 4][row][4 * (lane & 15)]);
+      __builtin_nontemporal_store(v, reinterpret_cast<f4v*>(yrow + row * cols));
+    }
+    __syncthreads();  // the tile is rewritten for the next block-row
+  }
+}
+
 struct Launch {
   dim3 grid;
   int64_t n_runs;
@@ -378,10 +441,22 @@ hipError_t launch_quantize_axis0(const float* x, void* codes, uint8_t* scales, i
 
 hipError_t launch_dequantize_axis0(const void* codes, const uint8_t* scales, float* y,
                                    int64_t rows, int64_t cols, int elem, hipStream_t stream) {
+  const uint8_t* c = static_cast<const uint8_t*>(codes);
+  if (cols % (64 * kTileStrips) == 0 && rows % (32 * kTileRun) == 0 &&
+      (reinterpret_cast<uintptr_t>(scales) & 3) == 0) {
+    const int64_t wgs = (cols / (64 * kTileStrips)) * (rows / (32 * kTileRun));
+    if (wgs > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (elem == kE2M1)
+      hipLaunchKernelGGL(dequantize_axis0_tile_kernel<kE2M1>, dim3((unsigned)wgs),
+                         dim3(64 * kTileStrips), 0, stream, c, scales, y, rows, cols);
+    else
+      hipLaunchKernelGGL(dequantize_axis0_tile_kernel<kE4M3>, dim3((unsigned)wgs),
+                         dim3(64 * kTileStrips), 0, stream, c, scales, y, rows, cols);
+    return hipGetLastError();
+  }
   const Launch l = plan(scales, rows, cols);
   if (l.grid.x == 0 || (int64_t)l.grid.x * (kThreads / 64) < ((cols + 63) / 64) * l.n_runs)
     return hipErrorInvalidValue;
-  const uint8_t* c = static_cast<const uint8_t*>(codes);
   if (elem == kE2M1)
     hipLaunchKernelGGL(dequantize_axis0_kernel<kE2M1>, l.grid, dim3(kThreads), 0, stream, c,
                        scales, y, rows, cols, l.scale_vec);

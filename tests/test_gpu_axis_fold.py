@@ -96,6 +96,34 @@ def test_dequantize_axis0_every_code_and_byte(elem):
 
 
 @pytest.mark.parametrize("elem", ELEMS)
+def test_dequantize_axis0_tile_path(elem):
+    """Shapes the workgroup-tiled decode takes (columns a multiple of 256,
+    rows of 128): every code in every column and block-row position, scale
+    bytes across the E8M0 range (0, subnormal results, 254, the 0xFF NaN
+    byte), a scale array 4 bytes off a 16-byte boundary, and guard floats
+    around the output."""
+    n_codes = 16 if elem == O.E2M1 else 256
+    bytes_ = np.array([0, 1, 2, 100, 126, 127, 128, 200, 252, 253, 254, 255], np.uint8)
+    rows, cols = 32 * len(bytes_), 512
+    c_idx = np.arange(cols)[:, None]
+    r_idx = np.arange(rows)[None, :]
+    el = ((c_idx + 7 * r_idx) % n_codes).astype(np.uint8)                      # [cols, rows]
+    codes = O.pack_nibbles(el) if elem == O.E2M1 else el
+    scales = bytes_[(np.arange(len(bytes_))[None, :] + np.arange(cols)[:, None]) % len(bytes_)]
+    want = O.dequantize_axis0(codes, scales, elem, rows)
+    cd = dev(np.ascontiguousarray(codes))
+    sbuf = torch.full((scales.size + 8,), 0x33, dtype=torch.uint8, device="cuda")
+    sbuf[4:4 + scales.size] = dev(scales.reshape(-1))
+    ybuf = torch.full((rows * cols + 32,), -7.0, dtype=torch.float32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    B.mx_dequantize_axis(cd.data_ptr(), sbuf.data_ptr() + 4, ybuf.data_ptr() + 64, rows, cols, 0,
+                         elem, 32, stream)
+    yb = host(ybuf)
+    assert (yb[:16] == -7.0).all() and (yb[16 + rows * cols:] == -7.0).all()
+    assert_bits_equal(yb[16:16 + rows * cols].reshape(rows, cols), want, "dequantize axis 0 tile")
+
+
+@pytest.mark.parametrize("elem", ELEMS)
 @pytest.mark.parametrize("rows,cols", [(32, 3), (96, 65), (256, 128), (800, 40)])
 def test_dequantize_axis0_random(elem, rows, cols):
     rng = np.random.default_rng(rows + cols * 3 + elem)
