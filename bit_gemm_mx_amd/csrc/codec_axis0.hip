@@ -254,12 +254,18 @@ quantize_axis0_band_kernel(const float* __restrict__ x, uint8_t* __restrict__ co
     const int64_t b0 = band * kBandBlocks;                 // first block-row of the band
     constexpr int kChunks = kColBytes / 16;                // 16-byte chunks per column
     constexpr int kColsPerPass = kBandThreads / kChunks;
+    // Codes leave non-temporally: blocks along axis 0 are the weight side of
+    // a product, read later by a matmul rather than right away, and the
+    // streamed stores measured 54.0 -> 52.7 us (8192x8192 E2M1, rotating
+    // outputs).  The 32-byte scale pieces keep ordinary stores: four
+    // workgroups fill each 128-byte line, merged in L2 (non-temporal: 54.8).
 #pragma unroll
     for (int p = 0; p < 64 / kColsPerPass; ++p) {
       const int col = p * kColsPerPass + threadIdx.x / kChunks, ch = threadIdx.x % kChunks;
       if (c0 + col < cols)
-        *reinterpret_cast<u4v*>(codes + (c0 + col) * row_bytes + b0 * kBlockBytes + 16 * ch) =
-            *reinterpret_cast<const u4v*>(lc + col * kStride + 16 * ch);
+        __builtin_nontemporal_store(
+            *reinterpret_cast<const u4v*>(lc + col * kStride + 16 * ch),
+            reinterpret_cast<u4v*>(codes + (c0 + col) * row_bytes + b0 * kBlockBytes + 16 * ch));
     }
     // 32 scale bytes per column: two 16-byte stores
     const int sc = threadIdx.x / 2, half = threadIdx.x & 1;
