@@ -474,13 +474,14 @@ block_matmul_tiled(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa
   __shared__ __attribute__((aligned(1024))) uint8_t scales1[DW ? 16 : kScaleBytes];
 
   // Tile order: the hardware deals workgroups round-robin to the 8 XCDs, so
-  // give each XCD a contiguous range of tiles, walked in groups of up to 8
+  // give each XCD a contiguous range of tiles, walked in groups of up to 4
   // tile-rows so that concurrently running tiles share A rows and B columns
-  // in that XCD's L2.
+  // in that XCD's L2 (groups of 4 measured ~2% faster than 8 on the 8192^3
+  // FP8 product and the prefill product, 2 about the same, 16 7% slower).
   const int nwg = tiles_m * tiles_n;
   int pid = blockIdx.x;
   if ((nwg & 7) == 0) pid = (pid & 7) * (nwg >> 3) + (pid >> 3);
-  constexpr int kGroup = 8;
+  constexpr int kGroup = 4;
   const int in_group = kGroup * tiles_n;
   const int first_m = (pid / in_group) * kGroup;
   const int gsize = min(tiles_m - first_m, kGroup);
