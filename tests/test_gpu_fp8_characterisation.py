@@ -12,13 +12,20 @@ or with random codes, T1 is exceeded on a fraction of the outputs.  These
 tests print that fraction and the worst ratio, and check only what the
 measured arithmetic guarantees: identical NaN positions and an error within
 T1 plus the truncation bound of gpu_util.fp8_group_truncation_bound.
+
+The last test is parity proper: the same E4M3 x E4M3 products taken through
+the library's other route -- B^T decoded along axis 0 to a float32 B
+(mx_dequantize_axis, exact) and multiplied by mx_block_matmul_f32b, whose
+products are exact (bf16 parts or fp32 matrix cores) -- are held to T1 on the
+very inputs where the single FP8 instruction is not.
 """
 import numpy as np
 import pytest
 
+from bit_gemm_mx_amd import binding as B
 from oracle import mx_oracle as O
 
-from gpu_util import fp8_group_truncation_bound, gpu_matmul
+from gpu_util import assert_matmul_close, dev, fp8_group_truncation_bound, gpu_matmul, host
 from test_gpu_matmul import SHAPES, quantized_normal, rand_operand
 
 pytestmark = pytest.mark.gpu
@@ -56,3 +63,25 @@ def test_fp8_random_codes(M, N, K):
     got = gpu_matmul(ac, asc, O.E4M3, bc, bsc, O.E4M3, M, N, K)
     want, mag = O.block_matmul(ac, asc, O.E4M3, bc, bsc, O.E4M3, M, N, K)
     _characterise(f"E4M3xE4M3 random codes {M}x{N}x{K}", got, want, mag, ac, asc, bc, bsc, K)
+
+
+@pytest.mark.parametrize("kind", ["outliers", "random codes"])
+@pytest.mark.parametrize("M,N,K", SHAPES + [(2048, 1024, 3072)])
+def test_fp8_inputs_through_f32b_route_meet_t1(kind, M, N, K):
+    """E4M3 x E4M3 within T1 on every output, by B^T -> float32 B (axis-0
+    decode) and the f32-B product; (2048, 1024, 3072) takes its bf16-split
+    kernel, the other shapes its fp32-matrix-core kernels."""
+    rng = np.random.default_rng(M * 1000 + N * 10 + K + 8)
+    if kind == "outliers":
+        ac, asc = quantized_normal(rng, M, K, O.E4M3)
+        bc, bsc = quantized_normal(rng, N, K, O.E4M3)
+    else:
+        ac, asc = rand_operand(rng, M, K, O.E4M3)
+        bc, bsc = rand_operand(rng, N, K, O.E4M3)
+    # B^T [N, K] blocked along K is B [K, N] blocked along axis 0: same storage
+    b32 = B.dequantize(B.MXTensor(dev(bc), dev(bsc), K, N, O.E4M3, axis=0))
+    a = B.MXTensor(dev(ac), dev(asc), M, K, O.E4M3)
+    got = host(B.block_matmul_f32b(a, b32))
+    want, mag = O.block_matmul(ac, asc, O.E4M3, bc, bsc, O.E4M3, M, N, K)
+    worst = assert_matmul_close(got, want, mag)
+    print(f"E4M3xE4M3 {kind} {M}x{N}x{K} through the f32-B route: worst err/T1 {worst:.3g}")
