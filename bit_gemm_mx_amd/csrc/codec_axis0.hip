@@ -186,9 +186,10 @@ quantize_axis0_kernel(const float* __restrict__ x, uint8_t* __restrict__ codes,
 // passes the next barrier only after its own stores).  Tasks (band, strip)
 // are numbered band-major and workgroup b takes tasks kStrips*b .. +kStrips-1,
 // so the workgroups in flight write whole columns of codes and read every
-// fourth 256-byte piece of all rows.  8192x8192 E2M1 on one box: 53.2 us
-// against 57.0 us for eight waves of four block-rows on one strip per
-// workgroup (the quantize with its stores removed reads its input in
+// fourth 256-byte piece of all rows.  8192x8192 E2M1 on one box: 52.8 us
+// (53.2 before the non-temporal code stores below) against 57.0 us for eight
+// waves of four block-rows on one strip per workgroup (the quantize with its
+// stores removed reads its input in
 // 40.8 us; the stores, written contiguously instead of block-major, would
 // take 53.9 us in that kernel -- it is the write stream mixed into the reads
 // that costs, more than its layout).  Needs rows % 1024 == 0 and 16-byte
