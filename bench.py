@@ -165,24 +165,21 @@ def bench_codec(mx, W, torch, steps, warmup, ref=None):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     # Per-kernel durations: each kernel alone, `steps` back-to-back launches
-    # (rotating over the copies) between one pair of HIP events on the stream
-    # the kernels run on, so that the event overhead is not charged per launch.
-    timer = EventTimer(torch)
+    # rotating over the copies, captured in a HIP graph and replayed between
+    # HIP events on the stream the kernels run on (timed(), as for the parts),
+    # so that neither the event overhead nor the host's launch path is
+    # charged per launch.
+    n = [0]
 
-    def q_only():
-        for i in range(steps):
-            mx.quantize(xs[i % copies], mx.MX_E2M1, out=qs[i % copies])
+    def rot():
+        n[0] += 1
+        return n[0] % copies
 
-    def d_only():
-        for i in range(steps):
-            mx.dequantize(qs[i % copies], out=ys[i % copies])
-
-    timer.run("quantize", q_only)
-    timer.run("dequantize", d_only)
-    torch.cuda.synchronize()
+    q_ms, q_min = timed(torch, "quantize",
+                        lambda: (lambda j: mx.quantize(xs[j], mx.MX_E2M1, out=qs[j]))(rot()), steps)
+    d_ms, d_min = timed(torch, "dequantize",
+                        lambda: (lambda j: mx.dequantize(qs[j], out=ys[j]))(rot()), steps)
     per_op = codec_bytes(rows, cols, 0.5)
-    q_ms, q_min = (v / steps for v in timer.mean_ms("quantize"))
-    d_ms, d_min = (v / steps for v in timer.mean_ms("dequantize"))
     kernels = {
         "quantize_e2m1": dict(ms=q_ms, min_ms=q_min, bytes=per_op, src="quantize.hip",
                               kernel="quantize_kernel<1>"),
