@@ -68,6 +68,14 @@ def test_special_values(elem):
     codes, scales = check_quantize(x, elem, "special")
     y = gpu_dequantize(codes, scales, elem, 32)
     assert_bits_equal(y, O.dequantize(codes, scales, elem, 32), "dequantize special")
+    # The same blocks inside a tensor of whole wave iterations (2560 blocks,
+    # a multiple of 32), where the quantize stages codes and scale bytes
+    # through LDS: placed at iteration boundaries among Gaussian blocks.
+    rng = np.random.default_rng(elem)
+    big = (rng.standard_normal((2560, 32)) * np.exp2(rng.integers(-30, 30, (2560, 1)))).astype(np.float32)
+    at = [0, 1, 7, 8, 31, 32, 33, 255, 256, 511, 1000, 1023, 1024, 2000, 2047, 2558, 2559][:len(rows)]
+    big[at] = x[:len(at)]
+    check_quantize(big.reshape(64, 40 * 32), elem, "special, staged stores")
 
 
 def _sweep_values(lo_bits, hi_bits, stride, grid):
