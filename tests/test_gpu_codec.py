@@ -200,6 +200,50 @@ def test_e2m1_exhaustive_sweep():
         print(f"exhaustive E2M1 sweep: blocks {r0}..{min(nb, r0 + step)} of {nb} match", flush=True)
 
 
+def test_e4m3_exhaustive_sweep():
+    """Every float32 in [2^-10, 512), both signs (318,767,104 values), 31 per
+    block after an anchor (511) forcing e = 0, so each code must be the
+    nearest E4M3 grid magnitude of |x| itself ("Bit Layout", "Reference
+    encode and decode": nearest grid entry, the smaller on a tie, saturating
+    at the top).  Checked against that rule in closed form: the f8E4M3FN
+    magnitudes from their bit formula ((1 + m/8) 2^(e-7), subnormals m 2^-9),
+    and the expected index = the number of grid midpoints strictly below
+    |x| (np.searchsorted, side "left": a value on a midpoint takes the
+    smaller index), sign bit 0x80 for x < 0."""
+    lo, hi = 0x3A800000, 0x44000000
+    allv = np.arange(lo, hi, dtype=np.uint32).view(np.float32)
+    vals = np.concatenate([allv, -allv])
+    del allv
+    n_vals = vals.size
+    nb = -(-n_vals // 31)
+    flat = np.zeros(nb * 31, np.float32)                # zero pads after the last value
+    flat[:n_vals] = vals
+    del vals
+    x = np.empty((nb, 32), np.float32)
+    x[:, 0] = 511.0
+    x[:, 1:] = flat.reshape(nb, 31)
+    del flat
+    gc, gs = gpu_quantize(x, O.E4M3)
+    assert np.all(gs == 127)
+    assert np.all(gc[:, 0] == 0x7E)                     # 511 saturates to 448
+    c = np.arange(127)
+    e, m = c >> 3, (c & 7).astype(np.float64)
+    grid = np.where(e == 0, m * 2.0 ** -9, (1 + m / 8) * np.exp2(e.astype(np.float64) - 7))
+    assert grid[-1] == 448.0 and np.all(np.diff(grid) > 0)
+    mids = (grid[:-1] + grid[1:]) / 2                   # exact in float64
+    step = 1 << 20
+    for r0 in range(0, nb, step):
+        xs = x[r0:r0 + step, 1:]
+        mag = np.searchsorted(mids, np.abs(xs.astype(np.float64)), side="left")
+        want = (mag | np.where(xs < 0, 0x80, 0)).astype(np.uint8)
+        got = gc[r0:r0 + step, 1:]
+        bad = np.argwhere(got != want)
+        assert bad.size == 0, (f"blocks {r0}..: {len(bad)} codes differ, first x="
+                               f"{xs[tuple(bad[0])]!r} code {got[tuple(bad[0])]:#x} want "
+                               f"{want[tuple(bad[0])]:#x}")
+    print(f"exhaustive E4M3 sweep: {n_vals} values in {nb} blocks match the rounding rule", flush=True)
+
+
 @pytest.mark.parametrize("elem", ELEMS)
 def test_exhaustive_decode(elem):
     if elem == O.E2M1:
