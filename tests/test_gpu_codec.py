@@ -13,6 +13,7 @@ from bit_gemm_mx_amd import binding as B
 from bit_gemm_mx_amd import workloads as W
 from oracle import mx_oracle as O
 
+from closed_forms import e4m3_codes_at_unit_scale
 from gpu_util import assert_bits_equal, dev, gpu_dequantize, gpu_quantize, host
 
 pytestmark = pytest.mark.gpu
@@ -205,11 +206,9 @@ def test_e4m3_exhaustive_sweep():
     block after an anchor (511) forcing e = 0, so each code must be the
     nearest E4M3 grid magnitude of |x| itself ("Bit Layout", "Reference
     encode and decode": nearest grid entry, the smaller on a tie, saturating
-    at the top).  Checked against that rule in closed form: the f8E4M3FN
-    magnitudes from their bit formula ((1 + m/8) 2^(e-7), subnormals m 2^-9),
-    and the expected index = the number of grid midpoints strictly below
-    |x| (np.searchsorted, side "left": a value on a midpoint takes the
-    smaller index), sign bit 0x80 for x < 0."""
+    at the top).  Checked against that rule in closed form
+    (closed_forms.e4m3_codes_at_unit_scale, itself checked against the oracle
+    in test_oracle_quantize.py)."""
     lo, hi = 0x3A800000, 0x44000000
     allv = np.arange(lo, hi, dtype=np.uint32).view(np.float32)
     vals = np.concatenate([allv, -allv])
@@ -226,16 +225,10 @@ def test_e4m3_exhaustive_sweep():
     gc, gs = gpu_quantize(x, O.E4M3)
     assert np.all(gs == 127)
     assert np.all(gc[:, 0] == 0x7E)                     # 511 saturates to 448
-    c = np.arange(127)
-    e, m = c >> 3, (c & 7).astype(np.float64)
-    grid = np.where(e == 0, m * 2.0 ** -9, (1 + m / 8) * np.exp2(e.astype(np.float64) - 7))
-    assert grid[-1] == 448.0 and np.all(np.diff(grid) > 0)
-    mids = (grid[:-1] + grid[1:]) / 2                   # exact in float64
     step = 1 << 20
     for r0 in range(0, nb, step):
         xs = x[r0:r0 + step, 1:]
-        mag = np.searchsorted(mids, np.abs(xs.astype(np.float64)), side="left")
-        want = (mag | np.where(xs < 0, 0x80, 0)).astype(np.uint8)
+        want = e4m3_codes_at_unit_scale(xs)
         got = gc[r0:r0 + step, 1:]
         bad = np.argwhere(got != want)
         assert bad.size == 0, (f"blocks {r0}..: {len(bad)} codes differ, first x="

@@ -316,3 +316,33 @@ def test_quantize_error_within_half_grid_step(elem):
     step = grid[j] - grid[j - 1]
     bound = np.where(t > grid[-1], t - grid[-1], step / 2) * scale
     assert np.all(np.abs(y - x) <= bound + 0.0)
+
+
+def test_e4m3_rounding_matches_closed_form():
+    """The oracle's E4M3 rounding (argmin over the grid) against the closed
+    form the exhaustive GPU sweep is checked with (grid from the f8E4M3FN bit
+    formula, index = number of grid midpoints strictly below |y|): random
+    float32 of both signs over [2^-10, 512), every midpoint and its float32
+    neighbours 1..4 ulp away, in blocks whose anchor 511 forces scale byte 127
+    (y = x).  Pins both: a wrong tie direction, grid entry or saturation in
+    either fails here."""
+    from closed_forms import e4m3_codes_at_unit_scale, e4m3_magnitudes
+    rng = np.random.default_rng(31)
+    bits = rng.integers(0x3A800000, 0x44000000, size=40000 * 31, dtype=np.uint32)
+    v = bits.view(np.float32) * np.where(rng.random(bits.size) < 0.5, -1, 1).astype(np.float32)
+    grid = e4m3_magnitudes()
+    mids = ((grid[:-1] + grid[1:]) / 2)
+    mids = mids[mids >= 2.0 ** -10].astype(np.float32)        # all exact in float32
+    near = np.concatenate([(mids.view(np.uint32).astype(np.int64) + d).astype(np.uint32)
+                           .view(np.float32) for d in range(-4, 5)])
+    v = np.concatenate([v, near, -near])
+    nb = -(-v.size // 31)
+    flat = np.full(nb * 31, np.float32(1.0))
+    flat[:v.size] = v
+    x = np.empty((nb, 32), np.float32)
+    x[:, 0] = 511.0
+    x[:, 1:] = flat.reshape(nb, 31)
+    codes, scales = O.quantize(x, O.E4M3)
+    assert np.all(scales == 127)
+    assert np.array_equal(codes[:, 1:], e4m3_codes_at_unit_scale(x[:, 1:]))
+    assert np.all(codes[:, 0] == 0x7E)
