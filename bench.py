@@ -765,8 +765,9 @@ def main():
     ap.add_argument("--no-codec", action="store_true",
                     help="skip the codec step (profiling the matmul workloads alone)")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a plain 256 MiB device-to-device copy, the reference that "
-                         "scales the FETCH_SIZE / WRITE_SIZE counters of a --pmc run")
+                    help="also run plain 1 GiB device-to-device copies up front (the size of "
+                         "the copy-context part), the reference that scales the FETCH_SIZE / "
+                         "WRITE_SIZE counters of a --pmc run")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): the MX hot path is "
@@ -789,7 +790,7 @@ def main():
     torch.cuda.set_device(0)
 
     if args.copy_calibration:
-        src = torch.empty(64 * 1024 * 1024, dtype=torch.float32, device="cuda").fill_(1.0)
+        src = torch.empty(256 * 1024 * 1024, dtype=torch.float32, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
