@@ -148,8 +148,14 @@ mx_status_t mx_block_matmul(const void *a_codes, const uint8_t *a_scales, mx_ele
  * in float32 precision: each product is rounded to float32 or (on the bf16
  * matrix cores, with B split into three exact bf16 parts) exact, partial
  * sums span at most 16 blocks before they are added in float32, and every
- * output lies within 1e-5 * sum_k |a_k b_k| of the exact value; a NaN scale
- * or E4M3 NaN code in row m of A makes row m of C NaN.
+ * output lies within 1e-5 * sum_k |a_k b_k| of the exact value (plus 2^-150
+ * for each product below the normal float32 range, which rounds to zero or a
+ * subnormal); a NaN scale
+ * or E4M3 NaN code in row m of A makes row m of C NaN.  A is decoded to
+ * float32 as mx_dequantize decodes it, so a code whose value exceeds the
+ * float32 range (possible only at scale bytes above 252 for E2M1 or 246 for
+ * E4M3, which mx_quantize never writes) is +-Inf there, and the outputs of
+ * its row are +-Inf or NaN even where the exact sum is finite.
  * Errors as mx_block_matmul (MX_ERR_ALIGN for a misaligned a_codes, b or c).
  */
 mx_status_t mx_block_matmul_f32b(const void *a_codes, const uint8_t *a_scales, mx_elem_t a_elem,
