@@ -109,6 +109,27 @@ def test_f32b_a_beyond_float32_decodes_to_infinity(elem):
     assert_matmul_close(got[~beyond], want[~beyond], mag[~beyond])
 
 
+@pytest.mark.parametrize("elem", [O.E2M1, O.E4M3])
+@pytest.mark.parametrize("M,N,K", [(70, 100, 1056), (2048, 1028, 384), (33, 4, 4352)])
+def test_f32b_products_below_the_normal_range(elem, M, N, K):
+    """The three f32-B kernels (fp32 matrix cores, bf16 split, streamed
+    K-split) with products far below the normal float32 range (A at scale
+    byte 30 times B = 2^-60: 2^-157 and smaller) beside ordinary ones: every
+    output within the stated tolerance plus the header's underflow term,
+    2^-146 per product."""
+    rng = np.random.default_rng(M + N + K + elem)
+    sa = np.array([127, 30, 100, 30])[np.arange(M) % 4]
+    ac, asc = uniform_operand(M, K, elem, sa)
+    b = np.where(rng.random((K, N)) < 0.5, 2.0 ** -60, 1.0).astype(np.float32)
+    b[:, ::3] *= -1
+    a = B.MXTensor(dev(ac), dev(asc), M, K, elem)
+    got = host(B.block_matmul_f32b(a, dev(b)))
+    want, mag = O.block_matmul_f32b(ac, asc, elem, b, M, N, K)
+    err = np.abs(got.astype(np.float64) - want)
+    bound = 1e-5 * mag + K * 2.0 ** -146
+    assert np.all(err <= bound), f"worst err / bound {np.max(err / bound):.3g}"
+
+
 SMALL = {O.E2M1: (0x1, 0.5), O.E4M3: (0x01, 2.0 ** -9)}   # smallest nonzero magnitudes
 
 
@@ -141,3 +162,31 @@ def test_scale_product_beyond_float32_with_small_codes(ae, be, M, N, K):
     want, mag = O.block_matmul(ac, asc, ae, bc, bsc, be, M, N, K)
     assert np.all(np.abs(want[:, 1:7][np.isfinite(want[:, 1:7])]) == 2.0 ** 127)
     check(got, want, mag)
+
+
+@pytest.mark.parametrize("ae,be", list(FIRST_INF))
+@pytest.mark.parametrize("M,N,K", [(16, 64, 1024), (17, 36, 1056), (300, 257, 1024),
+                                   (200, 70, 1056)])
+def test_outputs_in_the_float32_subnormal_range(ae, be, M, N, K):
+    """Scale bytes at the bottom of the E8M0 range: the exact outputs run
+    through the float32 subnormals (from below half the smallest one, zero,
+    for E2M1 x E2M1) to normal values.  Below the normal float32 range the
+    matrix instruction keeps each scaled contribution only on a grid near
+    the smallest subnormals (measured: at most 3.1 * 2^-149 per block of K
+    beyond the stated tolerance), so the bound here adds the header's
+    underflow term, 2^-146 per block.  Normal outputs hold the stated
+    tolerance alone."""
+    sa = 40 + 4 * (np.arange(M) % 8)
+    sb = 40 + 3 * (np.arange(N) % 8)
+    ac, asc = uniform_operand(M, K, ae, sa)
+    bc, bsc = uniform_operand(N, K, be, sb, negative_rows=range(1, N, 3))
+    got = gpu_matmul(ac, asc, ae, bc, bsc, be, M, N, K)
+    want, mag = O.block_matmul(ac, asc, ae, bc, bsc, be, M, N, K)
+    tiny = np.finfo(np.float32).tiny
+    sub = (want != 0) & (np.abs(want) < tiny)
+    assert sub.any() and (np.abs(want) >= tiny).any()
+    err = np.abs(got.astype(np.float64) - want)
+    bound = 1e-5 * mag + (K // 32) * 2.0 ** -146
+    assert np.all(err <= bound), f"worst err / bound {np.max(err / bound):.3g}"
+    nrm = np.abs(want) >= tiny
+    assert_matmul_close(got[nrm], want[nrm], mag[nrm])
