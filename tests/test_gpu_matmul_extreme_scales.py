@@ -190,3 +190,36 @@ def test_outputs_in_the_float32_subnormal_range(ae, be, M, N, K):
     assert np.all(err <= bound), f"worst err / bound {np.max(err / bound):.3g}"
     nrm = np.abs(want) >= tiny
     assert_matmul_close(got[nrm], want[nrm], mag[nrm])
+
+
+@pytest.mark.parametrize("ae,be", [(O.E4M3, O.E2M1), (O.E2M1, O.E2M1), (O.E4M3, O.E4M3)])
+def test_quantize_in_product_at_the_ends_of_float32(ae, be):
+    """mx_block_matmul_quantize_a with A rows near the largest float32
+    (scale bytes 246..252 from the quantize) and rows of subnormal floats
+    (scale bytes near 0), against B^T rows at scale bytes 127, 254 and 30:
+    outputs past the largest float32 are the same infinity, the others hold
+    the stated tolerance plus the underflow term.  (A's values span one
+    binade per block, so E4M3 x E4M3 groups stay inside the instruction's
+    exact window too; the subnormal rows quantize to zero codes at scale
+    byte 0.)"""
+    rng = np.random.default_rng(5 + ae + 3 * be)
+    M, N, K = 300, 257, 1024
+    fmax = float(np.finfo(np.float32).max)
+    kind = np.arange(M) % 3
+    a = rng.uniform(0.5, 1.0, (M, K))
+    a = np.where(kind[:, None] == 0, a * fmax, np.where(kind[:, None] == 1, a * 2.0 ** -140, a))
+    # one sign per output (A positive, signs from B's rows): where single
+    # products overflow float32, a sum of mixed signs would be order-dependent
+    a = a.astype(np.float32)
+    sb = np.array([127, 254, 30])[np.arange(N) % 3]
+    bc, bsc = uniform_operand(N, K, be, sb, negative_rows=range(1, N, 4))
+    bt = B.MXTensor(dev(bc), dev(bsc), N, K, be)
+    got = host(B.block_matmul_quantize_a(dev(a), ae, bt))
+    ac, asc = O.quantize(a, ae)
+    want, mag = O.block_matmul(ac, asc, ae, bc, bsc, be, M, N, K)
+    inf = np.isinf(want)
+    assert inf.any() and (~inf).any()
+    assert np.array_equal(got[inf], want[inf]), "an overflowing output is not the same infinity"
+    err = np.abs(got[~inf].astype(np.float64) - want[~inf])
+    bound = 1e-5 * mag[~inf] + (K // 32) * 2.0 ** -146
+    assert np.all(err <= bound), f"worst err / bound {np.max(err / bound):.3g}"
